@@ -1,0 +1,173 @@
+/*
+ * duolm.h -- C ABI of the MI355X (gfx950) DuoLM online ranker forward with
+ * multi-item scoring (MIS).
+ *
+ * What the library computes.  A request carries a shared user-history prefix
+ * of ids (instruction tokens, then per history item a marker token, one
+ * virtual-token-ID (VID) item vector and its feedback tokens) and K candidate
+ * VIDs.  The ranker (a Qwen3-0.6B-shaped decoder) prefills the prefix once;
+ * every candidate occupies one position, sits at logical position L (the
+ * prefix length) and attends to the prefix and to itself only, through a tree
+ * mask; a shared linear head turns the candidate's final hidden state into a
+ * score s = w^T h.  Nothing is decoded.  Sources:
+ *   - "DuoLM: Fast and Effective Personalized Recommendation with Language
+ *     Models" (paper.rainbus.top digest), sections 核心方法 (ranker input, shared
+ *     head, tree mask and unified position ids, the exactness identity) and
+ *     方法步骤详情 steps 3-5 (FP16 GPU-resident item table behind virtual ids
+ *     V + iota(i); requests carry only ids; prefix KV prefilled once and shared;
+ *     K scores returned in input order; graph replay of the segmented prefill);
+ *   - "DuoLM은 아이템 벡터 재사용과 공유 프리픽스로 LLM 추천 서빙을 가속한다"
+ *     (onedev.kr), sections 어떻게 동작하나 (input template, last hidden state,
+ *     no attention between candidates) and 어떻게 쓰나 (VID table appended after
+ *     the vocabulary V, packing after the shared prefix, tree mask plus
+ *     position-id rule, one prefill of the prefix KV per request).
+ *
+ * Conventions for every entry point:
+ *   - Return value: DUOLM_OK (0) or a negative duolm_status.  On error a
+ *     message is available from duolm_last_error() (thread-local), and no
+ *     output buffer has been written.
+ *   - The caller owns every buffer it passes; the library never keeps a
+ *     pointer to caller memory past the call.
+ *   - A ranker handle is used by one thread at a time.  Calls on one handle
+ *     are serialised on its stream.
+ *   - Scoring calls are synchronous: when they return, the scores are in the
+ *     output buffer.
+ */
+#ifndef DUOLM_H
+#define DUOLM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct duolm_ranker duolm_ranker; /* opaque, owned by the library */
+
+typedef enum {
+  DUOLM_OK = 0,
+  DUOLM_EINVAL = -1, /* bad argument: NULL pointer, K < 1, L < 1, length over a limit, bad option */
+  DUOLM_ERANGE = -2, /* an id outside [0, V + N) */
+  DUOLM_ENOMEM = -3, /* device or pinned-host allocation failed */
+  DUOLM_EHIP = -4,   /* a HIP runtime call failed */
+  DUOLM_EIO = -5,    /* weights file missing, short or malformed */
+  DUOLM_ESTATE = -6  /* call not valid in the handle's current state */
+} duolm_status;
+
+/* Model dimensions, read back from a loaded ranker. */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  float rms_eps, rope_base;
+  int64_t n_vid;      /* rows of the VID table now loaded (0 if none) */
+  int32_t max_prefix; /* largest accepted prefix length L */
+  int32_t max_rows;   /* largest number of rows one forward launch handles */
+} duolm_dims;
+
+/*
+ * Load ranker weights from a file written by this package's weights writer
+ * (magic "DUOLMW01", a 64-byte header with the dimensions, then the tensors in
+ * the canonical order, each 64-byte aligned; matrices bf16 [out, in], norm
+ * gains and the head vector fp32).  Weights are copied to device `hip_device`
+ * and re-laid-out for the kernels; the file is not kept open.
+ *   path   : NUL-terminated file path (host).
+ *   out    : receives the new handle; free it with duolm_free_ranker().
+ * Errors: EINVAL (NULL, unsupported dimensions), EIO, ENOMEM, EHIP.
+ */
+int duolm_load_ranker(const char* path, int hip_device, duolm_ranker** out);
+
+/* Same as duolm_load_ranker, from a host buffer holding the file's bytes. */
+int duolm_load_ranker_mem(const void* blob, uint64_t nbytes, int hip_device, duolm_ranker** out);
+
+/*
+ * Load (or replace) the item table D: n_rows fp16 rows of d_model values,
+ * row-major, host memory.  Row iota answers id V + iota (digest, 方法步骤详情
+ * step 3).  The rows are copied into a GPU-resident table.
+ * Errors: EINVAL (NULL, n_rows < 1, V + n_rows over INT32_MAX), ENOMEM, EHIP.
+ */
+int duolm_load_vid_table(duolm_ranker* r, const uint16_t* rows_fp16, int64_t n_rows);
+
+int duolm_get_dims(const duolm_ranker* r, duolm_dims* out);
+
+/* One request: prefix ids, then its candidate ids (host pointers). */
+typedef struct {
+  const int32_t* ids;      /* prefix_len ids, each in [0, V + N) */
+  int32_t prefix_len;      /* L >= 1 */
+  const int32_t* cand_ids; /* n_cand ids in [0, V + N) (VIDs in practice) */
+  int32_t n_cand;          /* K >= 1 */
+} duolm_request;
+
+typedef enum {
+  DUOLM_MODE_MIS = 0,        /* packed: prefix once, K one-row branches under the tree mask */
+  DUOLM_MODE_INDEPENDENT = 1 /* each candidate appended alone to the prefix, full causal forward */
+} duolm_mode;
+
+typedef struct {
+  int32_t mode;      /* duolm_mode */
+  int32_t use_graph; /* nonzero: replay a captured HIP graph for the batch's shape bucket */
+  void* hip_stream;  /* hipStream_t to order the work on, or NULL for the handle's own stream */
+} duolm_opts;
+
+/*
+ * Score a batch of requests (MIS by default).
+ *   reqs, n_req : n_req >= 1 requests (host).
+ *   scores      : host buffer of sum(n_cand) floats, written request-major,
+ *                 candidates in input order (digest, 方法步骤详情 step 4).
+ *   opts        : NULL means MIS with graph replay on the handle's stream.
+ * Ids are validated on the host before any device work.
+ * Errors: EINVAL, ERANGE, ESTATE (a VID id with no table loaded), ENOMEM, EHIP.
+ */
+int duolm_score_batch(duolm_ranker* r, const duolm_request* reqs, int32_t n_req, float* scores,
+                      const duolm_opts* opts);
+
+/*
+ * Device-resident variant: the ids are already in device memory.
+ *   prefix_len, n_cand : host arrays of n_req lengths.
+ *   d_ids              : device, int32, the requests concatenated as
+ *                        [prefix_0, cands_0, prefix_1, cands_1, ...].
+ *   d_scores           : device, sum(n_cand) floats, request-major.
+ * Ids are range-checked on the device: an out-of-range id makes the call
+ * return ERANGE with d_scores untouched.
+ */
+int duolm_score_batch_dev(duolm_ranker* r, const int32_t* prefix_len, const int32_t* n_cand, int32_t n_req,
+                          const int32_t* d_ids, float* d_scores, const duolm_opts* opts);
+
+/* Kernel classes for the profiling counters. */
+typedef enum {
+  DUOLM_K_EMBED = 0,      /* VID-aware embedding gather */
+  DUOLM_K_RMSNORM = 1,    /* input / post-attention RMSNorm */
+  DUOLM_K_GEMM_QKV = 2,   /* fused Q,K,V projection */
+  DUOLM_K_QK_ROPE = 3,    /* per-head q/k RMSNorm + rotary embedding */
+  DUOLM_K_ATTN_PREFIX = 4,/* causal attention over each prefix */
+  DUOLM_K_ATTN_BRANCH = 5,/* candidate-branch attention over the shared prefix KV + self */
+  DUOLM_K_GEMM_O = 6,     /* output projection + residual */
+  DUOLM_K_GEMM_GATEUP = 7,/* gate/up projection + SwiGLU */
+  DUOLM_K_GEMM_DOWN = 8,  /* down projection + residual */
+  DUOLM_K_HEAD = 9,       /* final RMSNorm + score head */
+  DUOLM_K_COUNT = 10
+} duolm_kernel_class;
+
+typedef struct {
+  int64_t launches;   /* launches timed since the last reset */
+  double total_ms;    /* sum of their HIP-event durations */
+  double flops;       /* algorithmic FLOPs of those launches (useful work only) */
+  double bytes;       /* algorithmic HBM bytes of those launches */
+} duolm_kernel_stats;
+
+/*
+ * Time launches of the kernel classes in `class_mask` (bit i = class i) with
+ * HIP events recorded on the launching stream, eager or inside captured
+ * graphs.  0 turns timing off.  Resets the counters.
+ */
+int duolm_set_profiling(duolm_ranker* r, uint32_t class_mask);
+int duolm_get_kernel_stats(duolm_ranker* r, int32_t kernel_class, duolm_kernel_stats* out);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* duolm_last_error(void);
+
+/* Frees weights, table, workspace, graphs and the handle.  NULL is a no-op. */
+void duolm_free_ranker(duolm_ranker* r);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DUOLM_H */

@@ -1,0 +1,264 @@
+"""ctypes binding of libduolm.so: one Python function per C entry point, same
+names, argument marshalling only.  All computation happens in the library's
+HIP kernels; there is no fallback path.  A missing library raises."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+try:  # torch's HIP runtime must be loaded first so the library binds to the same one
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover - torch is part of the image
+    torch = None
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libduolm.so")
+
+DUOLM_MODE_MIS = 0
+DUOLM_MODE_INDEPENDENT = 1
+
+KERNEL_CLASSES = ["embed", "rmsnorm", "gemm_qkv", "qk_rope", "attn_prefix", "attn_branch", "gemm_o",
+                  "gemm_gateup", "gemm_down", "head"]
+
+STAGES = {"attn_norm": 0, "qkv": 1, "qk_rope": 2, "attn": 3, "attn_resid": 4, "mlp_norm": 5, "swiglu": 6,
+          "layer_out": 7, "embed": 8}
+
+EPILOGUES = {"bf16": 0, "resid": 1, "swiglu": 2}
+
+STATUS = {0: "OK", -1: "EINVAL", -2: "ERANGE", -3: "ENOMEM", -4: "EHIP", -5: "EIO", -6: "ESTATE"}
+
+
+class DuolmError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+        self.status = STATUS.get(code, str(code))
+
+
+class duolm_dims(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ffn", C.c_int32), ("vocab", C.c_int32),
+                ("rms_eps", C.c_float), ("rope_base", C.c_float), ("n_vid", C.c_int64),
+                ("max_prefix", C.c_int32), ("max_rows", C.c_int32)]
+
+
+class duolm_request(C.Structure):
+    _fields_ = [("ids", C.POINTER(C.c_int32)), ("prefix_len", C.c_int32),
+                ("cand_ids", C.POINTER(C.c_int32)), ("n_cand", C.c_int32)]
+
+
+class duolm_opts(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("use_graph", C.c_int32), ("hip_stream", C.c_void_p)]
+
+
+class duolm_kernel_stats(C.Structure):
+    _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("flops", C.c_double), ("bytes", C.c_double)]
+
+
+_lib = None
+
+EXPORTS = {
+    "duolm_load_ranker": (C.c_int, [C.c_char_p, C.c_int, C.POINTER(C.c_void_p)]),
+    "duolm_load_ranker_mem": (C.c_int, [C.c_void_p, C.c_uint64, C.c_int, C.POINTER(C.c_void_p)]),
+    "duolm_load_vid_table": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64]),
+    "duolm_get_dims": (C.c_int, [C.c_void_p, C.POINTER(duolm_dims)]),
+    "duolm_score_batch": (C.c_int, [C.c_void_p, C.POINTER(duolm_request), C.c_int32, C.c_void_p,
+                                    C.POINTER(duolm_opts)]),
+    "duolm_score_batch_dev": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                        C.POINTER(duolm_opts)]),
+    "duolm_set_profiling": (C.c_int, [C.c_void_p, C.c_uint32]),
+    "duolm_get_kernel_stats": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(duolm_kernel_stats)]),
+    "duolm_last_error": (C.c_char_p, []),
+    "duolm_free_ranker": (None, [C.c_void_p]),
+    "duolm_debug_forward": (C.c_int, [C.c_void_p, C.POINTER(duolm_request), C.c_int32, C.c_int32, C.c_int32,
+                                      C.c_int32, C.c_void_p, C.c_uint64]),
+    "duolm_debug_gemm": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                   C.c_int32, C.c_void_p]),
+    "duolm_copy_device": (C.c_int, [C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p]),
+}
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m shared_prefix_scoring_amd.build)")
+        L = C.CDLL(LIB_PATH, mode=C.RTLD_GLOBAL)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise DuolmError(rc, lib().duolm_last_error().decode())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _requests(reqs: Sequence[Tuple[Iterable[int], Iterable[int]]]):
+    keep = []
+    arr = (duolm_request * len(reqs))()
+    for i, (prefix, cands) in enumerate(reqs):
+        p, c = _i32(prefix), _i32(cands)
+        keep += [p, c]
+        arr[i].ids = p.ctypes.data_as(C.POINTER(C.c_int32))
+        arr[i].prefix_len = p.shape[0]
+        arr[i].cand_ids = c.ctypes.data_as(C.POINTER(C.c_int32))
+        arr[i].n_cand = c.shape[0]
+    return arr, keep
+
+
+def _opts(mode: int, use_graph: bool, stream) -> duolm_opts:
+    return duolm_opts(int(mode), 1 if use_graph else 0, C.c_void_p(stream or 0))
+
+
+# ----------------------------------------------------------------- entry points
+
+def duolm_load_ranker(path: str, hip_device: int = 0) -> C.c_void_p:
+    h = C.c_void_p()
+    _check(lib().duolm_load_ranker(path.encode(), hip_device, C.byref(h)))
+    return h
+
+
+def duolm_load_ranker_mem(blob: np.ndarray, hip_device: int = 0) -> C.c_void_p:
+    b = np.ascontiguousarray(blob, dtype=np.uint8)
+    h = C.c_void_p()
+    _check(lib().duolm_load_ranker_mem(b.ctypes.data, b.nbytes, hip_device, C.byref(h)))
+    return h
+
+
+def duolm_load_vid_table(r, rows_fp16: np.ndarray) -> None:
+    rows = np.ascontiguousarray(rows_fp16, dtype=np.uint16)
+    if rows.ndim != 2:
+        raise ValueError("rows must be [n_rows, d_model]")
+    _check(lib().duolm_load_vid_table(r, rows.ctypes.data, rows.shape[0]))
+
+
+def duolm_get_dims(r) -> duolm_dims:
+    d = duolm_dims()
+    _check(lib().duolm_get_dims(r, C.byref(d)))
+    return d
+
+
+def duolm_score_batch(r, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None) -> np.ndarray:
+    arr, keep = _requests(reqs)
+    n = sum(int(np.asarray(c).shape[0]) for _, c in reqs)
+    out = np.empty(n, dtype=np.float32)
+    o = _opts(mode, use_graph, stream)
+    _check(lib().duolm_score_batch(r, arr, len(reqs), out.ctypes.data, C.byref(o)))
+    del keep
+    return out
+
+
+def duolm_score_batch_dev(r, prefix_len, n_cand, d_ids: int, d_scores: int, mode: int = DUOLM_MODE_MIS,
+                          use_graph: bool = True, stream=None) -> None:
+    L, K = _i32(prefix_len), _i32(n_cand)
+    o = _opts(mode, use_graph, stream)
+    _check(lib().duolm_score_batch_dev(r, L.ctypes.data, K.ctypes.data, L.shape[0], C.c_void_p(d_ids),
+                                       C.c_void_p(d_scores), C.byref(o)))
+
+
+def duolm_set_profiling(r, class_mask: int) -> None:
+    _check(lib().duolm_set_profiling(r, class_mask))
+
+
+def duolm_get_kernel_stats(r, kernel_class: int) -> duolm_kernel_stats:
+    s = duolm_kernel_stats()
+    _check(lib().duolm_get_kernel_stats(r, kernel_class, C.byref(s)))
+    return s
+
+
+def duolm_last_error() -> str:
+    return lib().duolm_last_error().decode()
+
+
+def duolm_free_ranker(r) -> None:
+    lib().duolm_free_ranker(r)
+
+
+def duolm_debug_forward(r, reqs, layer: int, stage: int, out: np.ndarray, mode: int = DUOLM_MODE_MIS) -> np.ndarray:
+    arr, keep = _requests(reqs)
+    _check(lib().duolm_debug_forward(r, arr, len(reqs), mode, layer, stage, out.ctypes.data, out.nbytes))
+    del keep
+    return out
+
+
+def duolm_debug_gemm(epilogue: int, d_A: int, d_W: int, d_C: int, M: int, N: int, K: int, stream=None) -> None:
+    _check(lib().duolm_debug_gemm(epilogue, C.c_void_p(d_A), C.c_void_p(d_W), C.c_void_p(d_C), M, N, K,
+                                  C.c_void_p(stream or 0)))
+
+
+def duolm_copy_device(d_dst: int, d_src: int, nbytes: int, stream=None) -> None:
+    _check(lib().duolm_copy_device(C.c_void_p(d_dst), C.c_void_p(d_src), nbytes, C.c_void_p(stream or 0)))
+
+
+# ----------------------------------------------------------------- convenience
+
+class Ranker:
+    """Owning wrapper around a ranker handle."""
+
+    def __init__(self, handle):
+        self.h = handle
+        self.dims = duolm_get_dims(handle)
+
+    @classmethod
+    def from_file(cls, path: str, device: int = 0) -> "Ranker":
+        return cls(duolm_load_ranker(path, device))
+
+    @classmethod
+    def from_blob(cls, blob: np.ndarray, device: int = 0) -> "Ranker":
+        return cls(duolm_load_ranker_mem(blob, device))
+
+    def load_vid_table(self, rows_fp16: np.ndarray) -> None:
+        duolm_load_vid_table(self.h, rows_fp16)
+        self.dims = duolm_get_dims(self.h)
+
+    def score(self, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None) -> np.ndarray:
+        return duolm_score_batch(self.h, reqs, mode, use_graph, stream)
+
+    def score_dev(self, prefix_len, n_cand, d_ids: int, d_scores: int, mode: int = DUOLM_MODE_MIS,
+                  use_graph: bool = True, stream=None) -> None:
+        duolm_score_batch_dev(self.h, prefix_len, n_cand, d_ids, d_scores, mode, use_graph, stream)
+
+    def stage(self, reqs, layer: int, stage: str, mode: int = DUOLM_MODE_MIS) -> np.ndarray:
+        d = self.dims
+        if mode == DUOLM_MODE_MIS:
+            T = sum(len(p) + len(c) for p, c in reqs)
+        else:
+            T = sum((len(p) + 1) * len(c) for p, c in reqs)
+        width, dt = {
+            "attn_norm": (d.d_model, np.uint16), "mlp_norm": (d.d_model, np.uint16),
+            "qkv": ((d.n_heads + 2 * d.n_kv_heads) * d.head_dim, np.uint16),
+            "qk_rope": ((d.n_heads + 2 * d.n_kv_heads) * d.head_dim, np.uint16),
+            "attn": (d.n_heads * d.head_dim, np.uint16), "swiglu": (d.d_ffn, np.uint16),
+        }.get(stage, (d.d_model, np.float32))
+        out = np.empty((T, width), dtype=dt)
+        return duolm_debug_forward(self.h, reqs, layer, STAGES[stage], out, mode)
+
+    def set_profiling(self, classes: Iterable[str]) -> None:
+        mask = 0
+        for c in classes:
+            mask |= 1 << KERNEL_CLASSES.index(c)
+        duolm_set_profiling(self.h, mask)
+
+    def kernel_stats(self, cls: str) -> duolm_kernel_stats:
+        return duolm_get_kernel_stats(self.h, KERNEL_CLASSES.index(cls))
+
+    def close(self) -> None:
+        if self.h:
+            duolm_free_ranker(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

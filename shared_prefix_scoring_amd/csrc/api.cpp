@@ -1,0 +1,1056 @@
+// C ABI and host executor of the DuoLM MIS ranker library.
+//
+// Per scoring call the executor
+//   1. validates the request lengths (and, for host ids, the id ranges),
+//   2. plans one or more forward launches: a launch is a set of sequences
+//      packed row after row, with its causal-attention tiles, its branch
+//      attention tiles and the rows the score head reads,
+//   3. uploads each launch's small descriptor block (CallHeader, sequence
+//      table, tile lists, head rows) from pinned memory,
+//   4. runs the forward -- embedding gather, n_layers x (RMSNorm, QKV GEMM,
+//      q/k norm + rotary, prefix attention, branch attention, O GEMM +
+//      residual, RMSNorm, gate/up GEMM + SwiGLU, down GEMM + residual), score
+//      head -- eagerly or by replaying a HIP graph captured for the launch's
+//      shape bucket (every kernel reads its true sizes from the descriptor,
+//      so only the descriptor and ids change between replays),
+//   5. synchronises, checks the device id-range flag, and copies the scores.
+#include <hip/hip_runtime.h>
+#include <fcntl.h>
+#include <sys/mman.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/duolm.h"
+#include "../../include/duolm_debug.h"
+#include "launch.h"
+
+using namespace duolm;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                \
+  do {                                                                               \
+    hipError_t e__ = (expr);                                                         \
+    if (e__ != hipSuccess) return fail(DUOLM_EHIP, "%s: %s", #expr, hipGetErrorString(e__)); \
+  } while (0)
+
+constexpr int64_t kDefaultMaxRows = 262144;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Bucket an upper bound: smallest m * 2^e >= x with m in [8, 16).
+int bucket(int x) {
+  if (x <= 16) return x <= 0 ? 0 : 16;
+  int e = 0;
+  while ((x >> e) >= 16) ++e;
+  int m = (x + (1 << e) - 1) >> e;
+  return m << e;
+}
+
+struct LayerW {
+  float* attn_norm;
+  uint16_t* wqkv;
+  float* q_norm;
+  float* k_norm;
+  uint16_t* wo;
+  float* mlp_norm;
+  uint16_t* wgu;
+  uint16_t* wdown;
+};
+
+// One forward launch.
+struct Plan {
+  int T = 0;
+  std::vector<int32_t> seq_row_off;
+  std::vector<SeqDesc> seqs;
+  std::vector<WorkItem> pitems, bitems;
+  std::vector<int32_t> head_rows;
+  int score_off = 0;
+};
+
+struct Caps {
+  int T, seq, pitems, bitems, scores;
+  bool operator<(const Caps& o) const {
+    return std::tie(T, seq, pitems, bitems, scores) < std::tie(o.T, o.seq, o.pitems, o.bitems, o.scores);
+  }
+};
+
+struct Timed {
+  int cls;
+  hipEvent_t a, b;
+};
+
+// A captured forward.  Without profiling it is one graph.  With profiling it
+// is split into segments so that every timed kernel is a graph of its own:
+// HIP events cannot time nodes inside a graph, but events recorded on the
+// stream between segment launches can.  cls is the kernel class a segment
+// times, or -1.
+struct GraphSeg {
+  hipGraphExec_t exec;
+  int cls;
+};
+struct GraphEntry {
+  std::vector<GraphSeg> segs;
+};
+
+}  // namespace
+
+struct duolm_ranker {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  duolm_dims dims{};
+  int nqkv = 0;  // (H + 2 Hkv) hd
+  int64_t max_rows = kDefaultMaxRows;
+  // weights
+  void* wblob = nullptr;
+  uint16_t* embed = nullptr;
+  std::vector<LayerW> layers;
+  float* final_norm = nullptr;
+  float* head = nullptr;
+  float2* rope = nullptr;
+  uint16_t* vid = nullptr;
+  int64_t n_vid = 0;
+  // activations
+  int cap_T = 0;
+  void* ws = nullptr;
+  float* X = nullptr;
+  uint16_t* Xn = nullptr;
+  uint16_t* QKV = nullptr;
+  uint16_t* Ob = nullptr;
+  uint16_t* Hb = nullptr;
+  int32_t* pos = nullptr;
+  // call inputs/outputs
+  int64_t cap_ids = 0;
+  int32_t* d_ids = nullptr;
+  int64_t cap_out = 0;
+  float* d_out = nullptr;
+  int32_t* d_err = nullptr;
+  int32_t* h_err = nullptr;  // pinned
+  // descriptor block
+  int cap_seq = 0, cap_pi = 0, cap_bi = 0, cap_hs = 0;
+  size_t off_sro = 0, off_seq = 0, off_pi = 0, off_bi = 0, off_hr = 0, meta_bytes = 0;
+  char* d_meta = nullptr;
+  char* h_meta[2] = {nullptr, nullptr};
+  hipEvent_t meta_free[2] = {nullptr, nullptr};
+  int meta_slot = 0;
+  // graphs
+  std::map<Caps, GraphEntry> graphs;
+  // profiling
+  uint32_t prof_mask = 0;
+  duolm_kernel_stats stats[DUOLM_K_COUNT]{};
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+};
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// weights file
+// ---------------------------------------------------------------------------
+struct FileHeader {
+  char magic[8];
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  float rms_eps, rope_base;
+  uint32_t reserved[5];
+};
+static_assert(sizeof(FileHeader) == 64, "file header");
+
+int check_dims(const FileHeader& h) {
+  if (memcmp(h.magic, "DUOLMW01", 8) != 0) return fail(DUOLM_EIO, "bad magic");
+  if (h.n_layers < 1 || h.d_model < 64 || h.n_heads < 1 || h.n_kv_heads < 1 || h.d_ffn < 32 || h.vocab < 1)
+    return fail(DUOLM_EINVAL, "bad dimensions in header");
+  if (h.n_heads % h.n_kv_heads != 0) return fail(DUOLM_EINVAL, "n_heads %% n_kv_heads != 0");
+  const int G = h.n_heads / h.n_kv_heads;
+  if (32 % G != 0) return fail(DUOLM_EINVAL, "query heads per KV head must divide 32");
+  if (!attn_supported(h.head_dim)) return fail(DUOLM_EINVAL, "head_dim must be 32, 64 or 128");
+  if (h.d_model % 64 || h.d_ffn % 64 || (h.n_heads * h.head_dim) % 64)
+    return fail(DUOLM_EINVAL, "d_model, d_ffn and n_heads*head_dim must be multiples of 64");
+  if (!(h.rms_eps >= 0.f) || !(h.rope_base > 1.f)) return fail(DUOLM_EINVAL, "bad eps / rope base");
+  return DUOLM_OK;
+}
+
+struct SrcTensor {
+  const void* p;
+  size_t bytes;
+};
+
+int parse_tensors(const FileHeader& h, const char* base, uint64_t nbytes, std::vector<SrcTensor>& out) {
+  const size_t d = h.d_model, hq = h.n_heads, hk = h.n_kv_heads, hd = h.head_dim, f = h.d_ffn;
+  std::vector<size_t> sizes;
+  sizes.push_back((size_t)h.vocab * d * 2);
+  for (int l = 0; l < h.n_layers; ++l) {
+    sizes.push_back(d * 4);            // attn_norm
+    sizes.push_back(hq * hd * d * 2);  // wq
+    sizes.push_back(hk * hd * d * 2);  // wk
+    sizes.push_back(hk * hd * d * 2);  // wv
+    sizes.push_back(hd * 4);           // q_norm
+    sizes.push_back(hd * 4);           // k_norm
+    sizes.push_back(d * hq * hd * 2);  // wo
+    sizes.push_back(d * 4);            // mlp_norm
+    sizes.push_back(f * d * 2);        // w_gate
+    sizes.push_back(f * d * 2);        // w_up
+    sizes.push_back(d * f * 2);        // w_down
+  }
+  sizes.push_back(d * 4);  // final_norm
+  sizes.push_back(d * 4);  // head
+  size_t off = 64;
+  out.clear();
+  for (size_t s : sizes) {
+    off = align_up(off, 64);
+    if (off + s > nbytes) return fail(DUOLM_EIO, "weights blob too short (%llu bytes)", (unsigned long long)nbytes);
+    out.push_back({base + off, s});
+    off += s;
+  }
+  return DUOLM_OK;
+}
+
+// Build the device weight image.  Q/K/V rows are concatenated into one
+// [(H + 2 Hkv) hd, d] matrix; gate and up rows are interleaved in 32-row
+// blocks (gate block p, up block p) so the gate/up GEMM's epilogue finds each
+// output column's gate and up values in the same lane.
+int load_weights(duolm_ranker* R, const FileHeader& h, const std::vector<SrcTensor>& src) {
+  const size_t d = h.d_model, hq = h.n_heads, hk = h.n_kv_heads, hd = h.head_dim, f = h.d_ffn;
+  const size_t nqkv = (hq + 2 * hk) * hd;
+  auto a = [](size_t x) { return align_up(x, 256); };
+  size_t total = a((size_t)h.vocab * d * 2);
+  const size_t per_layer = a(d * 4) + a(nqkv * d * 2) + a(hd * 4) * 2 + a(d * hq * hd * 2) + a(d * 4) +
+                           a(2 * f * d * 2) + a(d * f * 2);
+  total += per_layer * h.n_layers + a(d * 4) * 2 + a((size_t)kMaxPos * (hd / 2) * sizeof(float2));
+  HIP_TRY(hipMalloc(&R->wblob, total));
+  char* p = (char*)R->wblob;
+  auto take = [&](size_t bytes) {
+    char* q = p;
+    p += a(bytes);
+    return q;
+  };
+  size_t ti = 0;
+  R->embed = (uint16_t*)take((size_t)h.vocab * d * 2);
+  HIP_TRY(hipMemcpy(R->embed, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+  ++ti;
+  R->layers.resize(h.n_layers);
+  for (int l = 0; l < h.n_layers; ++l) {
+    LayerW& W = R->layers[l];
+    W.attn_norm = (float*)take(d * 4);
+    W.wqkv = (uint16_t*)take(nqkv * d * 2);
+    W.q_norm = (float*)take(hd * 4);
+    W.k_norm = (float*)take(hd * 4);
+    W.wo = (uint16_t*)take(d * hq * hd * 2);
+    W.mlp_norm = (float*)take(d * 4);
+    W.wgu = (uint16_t*)take(2 * f * d * 2);
+    W.wdown = (uint16_t*)take(d * f * 2);
+    HIP_TRY(hipMemcpy(W.attn_norm, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+    ++ti;
+    char* q = (char*)W.wqkv;
+    for (int k = 0; k < 3; ++k) {  // wq, wk, wv
+      HIP_TRY(hipMemcpy(q, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+      q += src[ti].bytes;
+      ++ti;
+    }
+    HIP_TRY(hipMemcpy(W.q_norm, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+    ++ti;
+    HIP_TRY(hipMemcpy(W.k_norm, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+    ++ti;
+    HIP_TRY(hipMemcpy(W.wo, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+    ++ti;
+    HIP_TRY(hipMemcpy(W.mlp_norm, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+    ++ti;
+    const size_t blk = 32 * d * 2;  // bytes of a 32-row block
+    // gate block p -> rows [64p, 64p + 32), up block p -> rows [64p + 32, 64p + 64)
+    HIP_TRY(hipMemcpy2D(W.wgu, 2 * blk, src[ti].p, blk, blk, f / 32, hipMemcpyHostToDevice));
+    ++ti;
+    HIP_TRY(hipMemcpy2D((char*)W.wgu + blk, 2 * blk, src[ti].p, blk, blk, f / 32, hipMemcpyHostToDevice));
+    ++ti;
+    HIP_TRY(hipMemcpy(W.wdown, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+    ++ti;
+  }
+  R->final_norm = (float*)take(d * 4);
+  HIP_TRY(hipMemcpy(R->final_norm, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+  ++ti;
+  R->head = (float*)take(d * 4);
+  HIP_TRY(hipMemcpy(R->head, src[ti].p, src[ti].bytes, hipMemcpyHostToDevice));
+  ++ti;
+  // rotary table: angle = pos * base^(-2i/hd), computed in double
+  const size_t half = hd / 2;
+  std::vector<float2> tab((size_t)kMaxPos * half);
+  for (size_t i = 0; i < half; ++i) {
+    const double inv_freq = std::pow((double)h.rope_base, -2.0 * (double)i / (double)hd);
+    for (int pp = 0; pp < kMaxPos; ++pp) {
+      const double ang = (double)pp * inv_freq;
+      tab[(size_t)pp * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  }
+  R->rope = (float2*)take(tab.size() * sizeof(float2));
+  HIP_TRY(hipMemcpy(R->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice));
+  return DUOLM_OK;
+}
+
+int create_from_blob(const void* blob, uint64_t nbytes, int dev, duolm_ranker** out) {
+  if (!blob || !out) return fail(DUOLM_EINVAL, "NULL argument");
+  if (nbytes < sizeof(FileHeader)) return fail(DUOLM_EIO, "weights blob shorter than its header");
+  FileHeader h;
+  memcpy(&h, blob, sizeof(h));
+  int rc = check_dims(h);
+  if (rc) return rc;
+  std::vector<SrcTensor> src;
+  rc = parse_tensors(h, (const char*)blob, nbytes, src);
+  if (rc) return rc;
+  int ndev = 0;
+  HIP_TRY(hipGetDeviceCount(&ndev));
+  if (dev < 0 || dev >= ndev) return fail(DUOLM_EINVAL, "hip_device %d out of range (%d devices)", dev, ndev);
+  HIP_TRY(hipSetDevice(dev));
+  duolm_ranker* R = new duolm_ranker();
+  R->device = dev;
+  R->dims.n_layers = h.n_layers;
+  R->dims.d_model = h.d_model;
+  R->dims.n_heads = h.n_heads;
+  R->dims.n_kv_heads = h.n_kv_heads;
+  R->dims.head_dim = h.head_dim;
+  R->dims.d_ffn = h.d_ffn;
+  R->dims.vocab = h.vocab;
+  R->dims.rms_eps = h.rms_eps;
+  R->dims.rope_base = h.rope_base;
+  R->dims.max_prefix = kMaxPos - 1;
+  R->nqkv = (h.n_heads + 2 * h.n_kv_heads) * h.head_dim;
+  if (const char* e = getenv("DUOLM_MAX_ROWS")) {
+    const long v = atol(e);
+    if (v >= 1024) R->max_rows = v;
+  }
+  R->dims.max_rows = (int32_t)R->max_rows;
+  rc = load_weights(R, h, src);
+  if (rc == DUOLM_OK) {
+    hipError_t e = hipStreamCreateWithFlags(&R->stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&R->h_err, sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc((void**)&R->d_err, sizeof(int32_t));
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&R->meta_free[0], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&R->meta_free[1], hipEventDisableTiming);
+    if (e != hipSuccess) rc = fail(DUOLM_EHIP, "stream/event setup: %s", hipGetErrorString(e));
+  }
+  if (rc != DUOLM_OK) {
+    duolm_free_ranker(R);
+    return rc;
+  }
+  *out = R;
+  return DUOLM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// capacities
+// ---------------------------------------------------------------------------
+void drop_graphs(duolm_ranker* R) {
+  for (auto& kv : R->graphs)
+    for (auto& sg : kv.second.segs)
+      if (sg.exec) (void)hipGraphExecDestroy(sg.exec);
+  R->graphs.clear();
+}
+
+int ensure_rows(duolm_ranker* R, int T) {
+  if (T <= R->cap_T) return DUOLM_OK;
+  HIP_TRY(hipStreamSynchronize(R->stream));
+  drop_graphs(R);
+  if (R->ws) (void)hipFree(R->ws);
+  R->ws = nullptr;
+  R->cap_T = 0;
+  const int cap = (int)std::min<int64_t>(R->max_rows, std::max<int64_t>(4096, align_up((size_t)T + T / 4, 4096)));
+  const auto& D = R->dims;
+  auto a = [](size_t x) { return align_up(x, 256); };
+  const size_t bX = a((size_t)cap * D.d_model * 4), bXn = a((size_t)cap * D.d_model * 2),
+               bQ = a((size_t)cap * R->nqkv * 2), bO = a((size_t)cap * D.n_heads * D.head_dim * 2),
+               bH = a((size_t)cap * D.d_ffn * 2), bP = a((size_t)cap * 4);
+  hipError_t e = hipMalloc(&R->ws, bX + bXn + bQ + bO + bH + bP);
+  if (e != hipSuccess) return fail(DUOLM_ENOMEM, "workspace for %d rows: %s", cap, hipGetErrorString(e));
+  char* p = (char*)R->ws;
+  R->X = (float*)p; p += bX;
+  R->Xn = (uint16_t*)p; p += bXn;
+  R->QKV = (uint16_t*)p; p += bQ;
+  R->Ob = (uint16_t*)p; p += bO;
+  R->Hb = (uint16_t*)p; p += bH;
+  R->pos = (int32_t*)p;
+  R->cap_T = cap;
+  return DUOLM_OK;
+}
+
+int ensure_meta(duolm_ranker* R, int n_seq, int n_pi, int n_bi, int n_hs) {
+  if (n_seq <= R->cap_seq && n_pi <= R->cap_pi && n_bi <= R->cap_bi && n_hs <= R->cap_hs) return DUOLM_OK;
+  HIP_TRY(hipStreamSynchronize(R->stream));
+  drop_graphs(R);
+  auto grow = [](int need, int have) { return std::max(have, std::max(256, (int)align_up((size_t)need * 5 / 4, 256))); };
+  R->cap_seq = grow(n_seq, R->cap_seq);
+  R->cap_pi = grow(n_pi, R->cap_pi);
+  R->cap_bi = grow(n_bi, R->cap_bi);
+  R->cap_hs = grow(n_hs, R->cap_hs);
+  size_t off = align_up(sizeof(CallHeader), 256);
+  R->off_sro = off; off = align_up(off + (size_t)(R->cap_seq + 1) * 4, 256);
+  R->off_seq = off; off = align_up(off + (size_t)R->cap_seq * sizeof(SeqDesc), 256);
+  R->off_pi = off; off = align_up(off + (size_t)R->cap_pi * sizeof(WorkItem), 256);
+  R->off_bi = off; off = align_up(off + (size_t)R->cap_bi * sizeof(WorkItem), 256);
+  R->off_hr = off; off = align_up(off + (size_t)R->cap_hs * 4, 256);
+  R->meta_bytes = off;
+  if (R->d_meta) (void)hipFree(R->d_meta);
+  for (auto& h : R->h_meta)
+    if (h) (void)hipHostFree(h);
+  R->d_meta = nullptr;
+  R->h_meta[0] = R->h_meta[1] = nullptr;
+  if (hipMalloc((void**)&R->d_meta, off) != hipSuccess || hipHostMalloc((void**)&R->h_meta[0], off) != hipSuccess ||
+      hipHostMalloc((void**)&R->h_meta[1], off) != hipSuccess) {
+    R->cap_seq = R->cap_pi = R->cap_bi = R->cap_hs = 0;
+    return fail(DUOLM_ENOMEM, "descriptor buffers (%zu bytes)", off);
+  }
+  return DUOLM_OK;
+}
+
+template <typename Tp>
+int ensure_buf(Tp*& ptr, int64_t& cap, int64_t need, hipStream_t s) {
+  if (need <= cap) return DUOLM_OK;
+  HIP_TRY(hipStreamSynchronize(s));
+  if (ptr) (void)hipFree(ptr);
+  ptr = nullptr;
+  cap = 0;
+  const int64_t n = std::max<int64_t>(need + need / 4, 4096);
+  if (hipMalloc((void**)&ptr, (size_t)n * sizeof(Tp)) != hipSuccess) return fail(DUOLM_ENOMEM, "device buffer");
+  cap = n;
+  return DUOLM_OK;
+}
+
+DevBatch dev_batch(duolm_ranker* R) {
+  DevBatch b;
+  b.hdr = (const CallHeader*)R->d_meta;
+  b.seq_row_off = (const int32_t*)(R->d_meta + R->off_sro);
+  b.seqs = (const SeqDesc*)(R->d_meta + R->off_seq);
+  b.pitems = (const WorkItem*)(R->d_meta + R->off_pi);
+  b.bitems = (const WorkItem*)(R->d_meta + R->off_bi);
+  b.head_rows = (const int32_t*)(R->d_meta + R->off_hr);
+  b.err = R->d_err;
+  return b;
+}
+
+// ---------------------------------------------------------------------------
+// planning
+// ---------------------------------------------------------------------------
+void plan_add_seq(duolm_ranker* R, Plan& P, int L, int K, int id_off, int id_len, int cand_id_off, bool head_last) {
+  const int G = R->dims.n_heads / R->dims.n_kv_heads;
+  const int s = (int)P.seqs.size();
+  SeqDesc sd{};
+  sd.row_off = P.T;
+  sd.L = L;
+  sd.K = K;
+  sd.id_off = id_off;
+  sd.id_len = id_len;
+  sd.cand_id_off = cand_id_off;
+  P.seqs.push_back(sd);
+  P.seq_row_off.push_back(P.T);
+  const int rp = attn_rows_per_item(false, G), rb = attn_rows_per_item(true, G);
+  for (int r0 = 0; r0 < L; r0 += rp) P.pitems.push_back({s, r0});
+  for (int c0 = 0; c0 < K; c0 += rb) P.bitems.push_back({s, c0});
+  if (head_last) P.head_rows.push_back(P.T + L - 1);
+  for (int j = 0; j < K; ++j) P.head_rows.push_back(P.T + L + j);
+  P.T += L + K;
+}
+
+void plan_close(Plan& P) { P.seq_row_off.push_back(P.T); }
+
+// Algorithmic FLOPs and bytes of one launch per kernel class.
+void launch_work(const duolm_ranker* R, const Plan& P, double fl[DUOLM_K_COUNT], double by[DUOLM_K_COUNT]) {
+  const auto& D = R->dims;
+  const double T = P.T, d = D.d_model, H = D.n_heads, Hk = D.n_kv_heads, hd = D.head_dim, F = D.d_ffn;
+  const double nq = R->nqkv;
+  for (int i = 0; i < DUOLM_K_COUNT; ++i) fl[i] = by[i] = 0;
+  by[DUOLM_K_EMBED] = T * (d * 2 + d * 4 + 8);
+  fl[DUOLM_K_RMSNORM] = T * d * 4;
+  by[DUOLM_K_RMSNORM] = T * (d * 4 + d * 2);
+  fl[DUOLM_K_GEMM_QKV] = 2 * T * d * nq;
+  by[DUOLM_K_GEMM_QKV] = (nq * d + T * d + T * nq) * 2;
+  by[DUOLM_K_QK_ROPE] = T * (H + Hk) * hd * 4 + T * 4;
+  fl[DUOLM_K_GEMM_O] = 2 * T * H * hd * d;
+  by[DUOLM_K_GEMM_O] = (d * H * hd + T * H * hd) * 2 + T * d * 8;
+  fl[DUOLM_K_GEMM_GATEUP] = 2 * T * d * 2 * F;
+  by[DUOLM_K_GEMM_GATEUP] = (2 * F * d + T * d + T * F) * 2;
+  fl[DUOLM_K_GEMM_DOWN] = 2 * T * F * d;
+  by[DUOLM_K_GEMM_DOWN] = (d * F + T * F) * 2 + T * d * 8;
+  for (const SeqDesc& s : P.seqs) {
+    const double L = s.L, K = s.K;
+    fl[DUOLM_K_ATTN_PREFIX] += 4 * hd * H * L * (L + 1) / 2;
+    by[DUOLM_K_ATTN_PREFIX] += L * (H * hd * 2 + Hk * hd * 4 + H * hd * 2);
+    fl[DUOLM_K_ATTN_BRANCH] += 4 * hd * H * K * (L + 1);
+    if (K > 0) by[DUOLM_K_ATTN_BRANCH] += L * Hk * hd * 4 + K * (H * hd * 2 + Hk * hd * 4 + H * hd * 2);
+  }
+  by[DUOLM_K_HEAD] = (double)P.head_rows.size() * (d * 4 + 4);
+  fl[DUOLM_K_HEAD] = (double)P.head_rows.size() * d * 4;
+}
+
+// ---------------------------------------------------------------------------
+// forward enqueue
+// ---------------------------------------------------------------------------
+hipEvent_t pool_event(duolm_ranker* R) {
+  if (R->ev_used == R->ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    R->ev_pool.push_back(e);
+  }
+  return R->ev_pool[R->ev_used++];
+}
+
+struct Enq {
+  duolm_ranker* R;
+  hipStream_t s;
+  std::vector<Timed>* timed;  // eager: where to record timing events (null: no timing)
+  GraphEntry* capture;        // graph capture in progress (null: eager)
+  int stop_layer = -1, stop_stage = -1;
+  bool stopped = false;
+  hipError_t cap_err = hipSuccess;
+
+  void end_segment(int cls) {
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(s, &g);
+    hipGraphExec_t ex = nullptr;
+    if (e == hipSuccess) e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    if (g) (void)hipGraphDestroy(g);
+    if (e == hipSuccess) capture->segs.push_back({ex, cls});
+    else if (cap_err == hipSuccess) cap_err = e;
+  }
+  void begin_segment() {
+    const hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess && cap_err == hipSuccess) cap_err = e;
+  }
+
+  template <typename F>
+  void run(int cls, F&& f) {
+    const bool want = R->prof_mask >> cls & 1u;
+    if (capture && want) {  // the timed kernel becomes a segment of its own
+      end_segment(-1);
+      begin_segment();
+      f();
+      end_segment(cls);
+      begin_segment();
+      return;
+    }
+    if (!capture && timed && want) {
+      hipEvent_t a = pool_event(R), b = pool_event(R);
+      if (a && b) {
+        (void)hipEventRecord(a, s);
+        f();
+        (void)hipEventRecord(b, s);
+        timed->push_back({cls, a, b});
+        return;
+      }
+    }
+    f();
+  }
+  bool stop(int layer, int stage) {
+    if (layer == stop_layer && stage == stop_stage) stopped = true;
+    return stopped;
+  }
+};
+
+void enqueue_forward(Enq& q, const Caps& c) {
+  duolm_ranker* R = q.R;
+  const auto& D = R->dims;
+  const int d = D.d_model, H = D.n_heads, Hk = D.n_kv_heads, hd = D.head_dim, F = D.d_ffn, nq = R->nqkv;
+  const float eps = D.rms_eps;
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+  hipStream_t s = q.s;
+  DevBatch b = dev_batch(R);
+  const int32_t* dT = &b.hdr->T;
+  q.run(DUOLM_K_EMBED, [&] { launch_embed(s, c.T, R->d_ids, b, R->embed, R->vid, D.vocab, R->n_vid, d, R->X, R->pos); });
+  if (q.stop(0, DUOLM_STAGE_EMBED)) return;
+  for (int l = 0; l < D.n_layers; ++l) {
+    const LayerW& W = R->layers[l];
+    q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, c.T, R->X, W.attn_norm, R->Xn, b.hdr, d, eps); });
+    if (q.stop(l, DUOLM_STAGE_ATTN_NORM)) return;
+    q.run(DUOLM_K_GEMM_QKV, [&] { launch_gemm(s, EPI_BF16, c.T, R->Xn, d, W.wqkv, d, R->QKV, nq, dT, nq, d); });
+    if (q.stop(l, DUOLM_STAGE_QKV)) return;
+    q.run(DUOLM_K_QK_ROPE, [&] {
+      launch_qk_rope(s, c.T, R->QKV, nq, b.hdr, R->pos, W.q_norm, W.k_norm, R->rope, H, Hk, hd, eps);
+    });
+    if (q.stop(l, DUOLM_STAGE_QK_ROPE)) return;
+    q.run(DUOLM_K_ATTN_PREFIX,
+          [&] { launch_attn(s, false, hd, c.pitems, R->QKV, nq, R->Ob, H * hd, b, H, Hk, scale_log2); });
+    if (c.bitems > 0)
+      q.run(DUOLM_K_ATTN_BRANCH,
+            [&] { launch_attn(s, true, hd, c.bitems, R->QKV, nq, R->Ob, H * hd, b, H, Hk, scale_log2); });
+    if (q.stop(l, DUOLM_STAGE_ATTN)) return;
+    q.run(DUOLM_K_GEMM_O, [&] { launch_gemm(s, EPI_RESID, c.T, R->Ob, H * hd, W.wo, H * hd, R->X, d, dT, d, H * hd); });
+    if (q.stop(l, DUOLM_STAGE_ATTN_RESID)) return;
+    q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, c.T, R->X, W.mlp_norm, R->Xn, b.hdr, d, eps); });
+    if (q.stop(l, DUOLM_STAGE_MLP_NORM)) return;
+    q.run(DUOLM_K_GEMM_GATEUP, [&] { launch_gemm(s, EPI_SWIGLU, c.T, R->Xn, d, W.wgu, d, R->Hb, F, dT, 2 * F, d); });
+    if (q.stop(l, DUOLM_STAGE_SWIGLU)) return;
+    q.run(DUOLM_K_GEMM_DOWN, [&] { launch_gemm(s, EPI_RESID, c.T, R->Hb, F, W.wdown, F, R->X, d, dT, d, F); });
+    if (q.stop(l, DUOLM_STAGE_LAYER_OUT)) return;
+  }
+  if (q.stop_layer >= 0) return;
+  q.run(DUOLM_K_HEAD, [&] { launch_head(s, c.scores, R->X, b, R->final_norm, R->head, R->d_out, d, eps); });
+}
+
+// Upload one launch's descriptor block (pinned double buffer).
+int upload_plan(duolm_ranker* R, const Plan& P, hipStream_t s) {
+  const int slot = R->meta_slot;
+  R->meta_slot ^= 1;
+  HIP_TRY(hipEventSynchronize(R->meta_free[slot]));
+  char* h = R->h_meta[slot];
+  CallHeader hdr{};
+  hdr.T = P.T;
+  hdr.n_seq = (int)P.seqs.size();
+  hdr.n_pitems = (int)P.pitems.size();
+  hdr.n_bitems = (int)P.bitems.size();
+  hdr.n_scores = (int)P.head_rows.size();
+  hdr.score_off = P.score_off;
+  memcpy(h, &hdr, sizeof(hdr));
+  memcpy(h + R->off_sro, P.seq_row_off.data(), P.seq_row_off.size() * 4);
+  memcpy(h + R->off_seq, P.seqs.data(), P.seqs.size() * sizeof(SeqDesc));
+  memcpy(h + R->off_pi, P.pitems.data(), P.pitems.size() * sizeof(WorkItem));
+  memcpy(h + R->off_bi, P.bitems.data(), P.bitems.size() * sizeof(WorkItem));
+  memcpy(h + R->off_hr, P.head_rows.data(), P.head_rows.size() * 4);
+  // copy up to the end of the last used section in one transfer when the gaps
+  // are small, else section by section
+  const size_t end_hr = R->off_hr + P.head_rows.size() * 4;
+  if (end_hr <= 256 * 1024) {
+    HIP_TRY(hipMemcpyAsync(R->d_meta, h, end_hr, hipMemcpyHostToDevice, s));
+  } else {
+    const size_t offs[6] = {0, R->off_sro, R->off_seq, R->off_pi, R->off_bi, R->off_hr};
+    const size_t lens[6] = {sizeof(CallHeader), P.seq_row_off.size() * 4, P.seqs.size() * sizeof(SeqDesc),
+                            P.pitems.size() * sizeof(WorkItem), P.bitems.size() * sizeof(WorkItem),
+                            P.head_rows.size() * 4};
+    for (int i = 0; i < 6; ++i)
+      if (lens[i]) HIP_TRY(hipMemcpyAsync(R->d_meta + offs[i], h + offs[i], lens[i], hipMemcpyHostToDevice, s));
+  }
+  HIP_TRY(hipEventRecord(R->meta_free[slot], s));
+  return DUOLM_OK;
+}
+
+void add_stats(duolm_ranker* R, const std::vector<Timed>& timed, const double fl[], const double by[]) {
+  for (const Timed& t : timed) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.a, t.b) != hipSuccess) continue;
+    duolm_kernel_stats& st = R->stats[t.cls];
+    st.launches += 1;
+    st.total_ms += ms;
+    st.flops += fl[t.cls];
+    st.bytes += by[t.cls];
+  }
+}
+
+// Run one planned launch: upload, then eager enqueue or graph replay.
+int run_launch(duolm_ranker* R, const Plan& P, hipStream_t s, bool use_graph, std::vector<Timed>* timed) {
+  int rc = upload_plan(R, P, s);
+  if (rc) return rc;
+  if (!use_graph) {
+    Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size()};
+    Enq q{R, s, R->prof_mask ? timed : nullptr, nullptr};
+    enqueue_forward(q, c);
+    HIP_TRY(hipGetLastError());
+    return DUOLM_OK;
+  }
+  Caps c{std::min(bucket(P.T), R->cap_T), std::min(bucket((int)P.seqs.size()), R->cap_seq),
+         std::min(bucket((int)P.pitems.size()), R->cap_pi), std::min(bucket((int)P.bitems.size()), R->cap_bi),
+         std::min(bucket((int)P.head_rows.size()), R->cap_hs)};
+  auto it = R->graphs.find(c);
+  if (it == R->graphs.end()) {
+    GraphEntry ge;
+    Enq q{R, s, nullptr, &ge};
+    q.begin_segment();
+    enqueue_forward(q, c);
+    q.end_segment(-1);
+    if (q.cap_err != hipSuccess) {
+      for (auto& sg : ge.segs) (void)hipGraphExecDestroy(sg.exec);
+      return fail(DUOLM_EHIP, "graph capture: %s", hipGetErrorString(q.cap_err));
+    }
+    it = R->graphs.emplace(c, std::move(ge)).first;
+  }
+  for (const GraphSeg& sg : it->second.segs) {
+    if (sg.cls >= 0 && timed) {
+      hipEvent_t a = pool_event(R), b = pool_event(R);
+      if (a && b) {
+        HIP_TRY(hipEventRecord(a, s));
+        HIP_TRY(hipGraphLaunch(sg.exec, s));
+        HIP_TRY(hipEventRecord(b, s));
+        timed->push_back({sg.cls, a, b});
+        continue;
+      }
+    }
+    HIP_TRY(hipGraphLaunch(sg.exec, s));
+  }
+  return DUOLM_OK;
+}
+
+struct CallInput {
+  const int32_t* prefix_len;
+  const int32_t* n_cand;
+  int n_req;
+};
+
+int validate_lengths(duolm_ranker* R, const CallInput& in, int64_t& total_ids, int64_t& total_scores) {
+  if (in.n_req < 1) return fail(DUOLM_EINVAL, "n_req must be >= 1");
+  total_ids = 0;
+  total_scores = 0;
+  for (int i = 0; i < in.n_req; ++i) {
+    const int L = in.prefix_len[i], K = in.n_cand[i];
+    if (L < 1) return fail(DUOLM_EINVAL, "request %d: prefix_len %d < 1", i, L);
+    if (K < 1) return fail(DUOLM_EINVAL, "request %d: n_cand %d < 1", i, K);
+    if (L > R->dims.max_prefix) return fail(DUOLM_EINVAL, "request %d: prefix_len %d over %d", i, L, R->dims.max_prefix);
+    if ((int64_t)L + K > R->max_rows)
+      return fail(DUOLM_EINVAL, "request %d: L + K = %d over the %lld-row launch limit", i, L + K,
+                  (long long)R->max_rows);
+    total_ids += L + K;
+    total_scores += K;
+  }
+  if (total_ids > INT32_MAX / 2) return fail(DUOLM_EINVAL, "batch too large");
+  return DUOLM_OK;
+}
+
+// Split the call into launches of at most max_rows rows.
+void build_plans(duolm_ranker* R, const CallInput& in, int mode, std::vector<Plan>& plans) {
+  plans.clear();
+  plans.emplace_back();
+  int64_t id_off = 0;
+  int score = 0;
+  for (int i = 0; i < in.n_req; ++i) {
+    const int L = in.prefix_len[i], K = in.n_cand[i];
+    if (mode == DUOLM_MODE_MIS) {
+      if (plans.back().T > 0 && plans.back().T + L + K > R->max_rows) {
+        plan_close(plans.back());
+        plans.emplace_back();
+        plans.back().score_off = score;
+      }
+      plan_add_seq(R, plans.back(), L, K, (int)id_off, L, (int)(id_off + L), false);
+    } else {
+      for (int j = 0; j < K; ++j) {
+        if (plans.back().T > 0 && plans.back().T + L + 1 > R->max_rows) {
+          plan_close(plans.back());
+          plans.emplace_back();
+          plans.back().score_off = score + j;
+        }
+        plan_add_seq(R, plans.back(), L + 1, 0, (int)id_off, L, (int)(id_off + L + j), true);
+      }
+    }
+    score += K;
+    id_off += L + K;
+  }
+  plan_close(plans.back());
+}
+
+int mode_ok(const duolm_opts* o) {
+  if (o && o->mode != DUOLM_MODE_MIS && o->mode != DUOLM_MODE_INDEPENDENT) return fail(DUOLM_EINVAL, "bad mode");
+  return DUOLM_OK;
+}
+
+// Shared body of the host and device entry points.  `ids` is host memory
+// when ids_dev is false.  Scores go to `out` (host or device).
+int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool ids_dev, float* out, bool out_dev,
+               const duolm_opts* opts) {
+  if (!R || !in.prefix_len || !in.n_cand || !ids || !out) return fail(DUOLM_EINVAL, "NULL argument");
+  int rc = mode_ok(opts);
+  if (rc) return rc;
+  const int mode = opts ? opts->mode : DUOLM_MODE_MIS;
+  const bool use_graph = opts ? opts->use_graph != 0 : true;
+  hipStream_t s = (opts && opts->hip_stream) ? (hipStream_t)opts->hip_stream : R->stream;
+  int64_t total_ids = 0, total_scores = 0;
+  rc = validate_lengths(R, in, total_ids, total_scores);
+  if (rc) return rc;
+  HIP_TRY(hipSetDevice(R->device));
+  if (!ids_dev) {
+    const int64_t lim = (int64_t)R->dims.vocab + R->n_vid;
+    for (int64_t i = 0; i < total_ids; ++i) {
+      const int32_t id = ids[i];
+      if (id < 0 || id >= lim) {
+        if (id >= R->dims.vocab && R->n_vid == 0 && id >= 0)
+          return fail(DUOLM_ESTATE, "id %d at position %lld is a VID but no item table is loaded", id, (long long)i);
+        return fail(DUOLM_ERANGE, "id %d at position %lld outside [0, %lld)", id, (long long)i, (long long)lim);
+      }
+    }
+  }
+  std::vector<Plan> plans;
+  build_plans(R, in, mode, plans);
+  int maxT = 0, mseq = 0, mpi = 0, mbi = 0, mhs = 0;
+  for (const Plan& P : plans) {
+    maxT = std::max(maxT, P.T);
+    mseq = std::max(mseq, (int)P.seqs.size());
+    mpi = std::max(mpi, (int)P.pitems.size());
+    mbi = std::max(mbi, (int)P.bitems.size());
+    mhs = std::max(mhs, (int)P.head_rows.size());
+  }
+  if ((rc = ensure_rows(R, maxT))) return rc;
+  if ((rc = ensure_meta(R, mseq, mpi, mbi, mhs))) return rc;
+  if ((rc = ensure_buf(R->d_ids, R->cap_ids, total_ids, R->stream))) return rc;
+  if ((rc = ensure_buf(R->d_out, R->cap_out, total_scores, R->stream))) return rc;
+  if (s != R->stream) HIP_TRY(hipStreamSynchronize(R->stream));
+  HIP_TRY(hipMemcpyAsync(R->d_ids, ids, (size_t)total_ids * 4,
+                         ids_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s));
+  *R->h_err = 0;
+  HIP_TRY(hipMemcpyAsync(R->d_err, R->h_err, 4, hipMemcpyHostToDevice, s));
+  R->ev_used = 0;
+  std::vector<Timed> timed_ev;
+  std::vector<std::pair<size_t, Plan const*>> plan_marks;  // timed_ev index where each plan starts
+  for (const Plan& P : plans) {
+    plan_marks.push_back({timed_ev.size(), &P});
+    if ((rc = run_launch(R, P, s, use_graph, &timed_ev))) {
+      (void)hipStreamSynchronize(s);
+      return rc;
+    }
+  }
+  HIP_TRY(hipMemcpyAsync(R->h_err, R->d_err, 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (R->prof_mask) {
+    double fl[DUOLM_K_COUNT], by[DUOLM_K_COUNT];
+    for (size_t i = 0; i < plan_marks.size(); ++i) {
+      const size_t end = i + 1 < plan_marks.size() ? plan_marks[i + 1].first : timed_ev.size();
+      launch_work(R, *plan_marks[i].second, fl, by);
+      std::vector<Timed> part(timed_ev.begin() + plan_marks[i].first, timed_ev.begin() + end);
+      add_stats(R, part, fl, by);
+    }
+  }
+  if (*R->h_err) return fail(DUOLM_ERANGE, "an id in the device batch is outside [0, V + N)");
+  HIP_TRY(hipMemcpyAsync(out, R->d_out, (size_t)total_scores * 4,
+                         out_dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return DUOLM_OK;
+}
+
+int flatten_requests(const duolm_request* reqs, int n_req, std::vector<int32_t>& L, std::vector<int32_t>& K,
+                     std::vector<int32_t>& ids) {
+  if (!reqs || n_req < 1) return fail(DUOLM_EINVAL, "need n_req >= 1 requests");
+  L.resize(n_req);
+  K.resize(n_req);
+  size_t total = 0;
+  for (int i = 0; i < n_req; ++i) {
+    if (reqs[i].prefix_len < 1 || reqs[i].n_cand < 1)
+      return fail(DUOLM_EINVAL, "request %d: prefix_len and n_cand must be >= 1", i);
+    if (!reqs[i].ids || !reqs[i].cand_ids) return fail(DUOLM_EINVAL, "request %d: NULL ids", i);
+    L[i] = reqs[i].prefix_len;
+    K[i] = reqs[i].n_cand;
+    total += (size_t)L[i] + K[i];
+  }
+  ids.resize(total);
+  size_t o = 0;
+  for (int i = 0; i < n_req; ++i) {
+    memcpy(&ids[o], reqs[i].ids, (size_t)L[i] * 4);
+    o += L[i];
+    memcpy(&ids[o], reqs[i].cand_ids, (size_t)K[i] * 4);
+    o += K[i];
+  }
+  return DUOLM_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+int duolm_load_ranker(const char* path, int hip_device, duolm_ranker** out) {
+  if (!path || !out) return fail(DUOLM_EINVAL, "NULL argument");
+  const int fd = open(path, O_RDONLY);
+  if (fd < 0) return fail(DUOLM_EIO, "cannot open %s", path);
+  struct stat st;
+  if (fstat(fd, &st) != 0 || st.st_size < 64) {
+    close(fd);
+    return fail(DUOLM_EIO, "cannot stat %s or file too short", path);
+  }
+  void* m = mmap(nullptr, (size_t)st.st_size, PROT_READ, MAP_PRIVATE, fd, 0);
+  close(fd);
+  if (m == MAP_FAILED) return fail(DUOLM_EIO, "cannot map %s", path);
+  const int rc = create_from_blob(m, (uint64_t)st.st_size, hip_device, out);
+  munmap(m, (size_t)st.st_size);
+  return rc;
+}
+
+int duolm_load_ranker_mem(const void* blob, uint64_t nbytes, int hip_device, duolm_ranker** out) {
+  return create_from_blob(blob, nbytes, hip_device, out);
+}
+
+int duolm_load_vid_table(duolm_ranker* R, const uint16_t* rows, int64_t n_rows) {
+  if (!R || !rows) return fail(DUOLM_EINVAL, "NULL argument");
+  if (n_rows < 1) return fail(DUOLM_EINVAL, "n_rows must be >= 1");
+  if ((int64_t)R->dims.vocab + n_rows > INT32_MAX) return fail(DUOLM_EINVAL, "V + n_rows exceeds int32 ids");
+  HIP_TRY(hipSetDevice(R->device));
+  HIP_TRY(hipStreamSynchronize(R->stream));
+  const size_t bytes = (size_t)n_rows * R->dims.d_model * 2;
+  uint16_t* p = nullptr;
+  if (hipMalloc((void**)&p, bytes) != hipSuccess) return fail(DUOLM_ENOMEM, "item table (%zu bytes)", bytes);
+  if (hipMemcpy(p, rows, bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(p);
+    return fail(DUOLM_EHIP, "item table upload failed");
+  }
+  if (R->vid) (void)hipFree(R->vid);
+  R->vid = p;
+  R->n_vid = n_rows;
+  R->dims.n_vid = n_rows;
+  drop_graphs(R);  // graphs bake the table pointer and size
+  return DUOLM_OK;
+}
+
+int duolm_get_dims(const duolm_ranker* R, duolm_dims* out) {
+  if (!R || !out) return fail(DUOLM_EINVAL, "NULL argument");
+  *out = R->dims;
+  return DUOLM_OK;
+}
+
+int duolm_score_batch(duolm_ranker* R, const duolm_request* reqs, int32_t n_req, float* scores,
+                      const duolm_opts* opts) {
+  if (!R || !scores) return fail(DUOLM_EINVAL, "NULL argument");
+  std::vector<int32_t> L, K, ids;
+  int rc = flatten_requests(reqs, n_req, L, K, ids);
+  if (rc) return rc;
+  CallInput in{L.data(), K.data(), n_req};
+  return score_impl(R, in, ids.data(), false, scores, false, opts);
+}
+
+int duolm_score_batch_dev(duolm_ranker* R, const int32_t* prefix_len, const int32_t* n_cand, int32_t n_req,
+                          const int32_t* d_ids, float* d_scores, const duolm_opts* opts) {
+  CallInput in{prefix_len, n_cand, n_req};
+  return score_impl(R, in, d_ids, true, d_scores, true, opts);
+}
+
+int duolm_set_profiling(duolm_ranker* R, uint32_t mask) {
+  if (!R) return fail(DUOLM_EINVAL, "NULL argument");
+  if (mask != R->prof_mask) drop_graphs(R);  // captured graphs carry their timing events
+  R->prof_mask = mask & ((1u << DUOLM_K_COUNT) - 1);
+  for (auto& st : R->stats) st = duolm_kernel_stats{};
+  return DUOLM_OK;
+}
+
+int duolm_get_kernel_stats(duolm_ranker* R, int32_t cls, duolm_kernel_stats* out) {
+  if (!R || !out) return fail(DUOLM_EINVAL, "NULL argument");
+  if (cls < 0 || cls >= DUOLM_K_COUNT) return fail(DUOLM_EINVAL, "bad kernel class %d", cls);
+  *out = R->stats[cls];
+  return DUOLM_OK;
+}
+
+const char* duolm_last_error(void) { return g_err.c_str(); }
+
+void duolm_free_ranker(duolm_ranker* R) {
+  if (!R) return;
+  (void)hipSetDevice(R->device);
+  if (R->stream) (void)hipStreamSynchronize(R->stream);
+  drop_graphs(R);
+  for (hipEvent_t e : R->ev_pool) (void)hipEventDestroy(e);
+  for (hipEvent_t e : R->meta_free)
+    if (e) (void)hipEventDestroy(e);
+  if (R->wblob) (void)hipFree(R->wblob);
+  if (R->vid) (void)hipFree(R->vid);
+  if (R->ws) (void)hipFree(R->ws);
+  if (R->d_ids) (void)hipFree(R->d_ids);
+  if (R->d_out) (void)hipFree(R->d_out);
+  if (R->d_err) (void)hipFree(R->d_err);
+  if (R->h_err) (void)hipHostFree(R->h_err);
+  if (R->d_meta) (void)hipFree(R->d_meta);
+  for (char* h : R->h_meta)
+    if (h) (void)hipHostFree(h);
+  if (R->stream) (void)hipStreamDestroy(R->stream);
+  delete R;
+}
+
+// ---------------------------------------------------------------------------
+// test support (duolm_debug.h)
+// ---------------------------------------------------------------------------
+int duolm_debug_forward(duolm_ranker* R, const duolm_request* reqs, int32_t n_req, int32_t mode, int32_t layer,
+                        int32_t stage, void* host_out, uint64_t nbytes) {
+  if (!R || !host_out) return fail(DUOLM_EINVAL, "NULL argument");
+  if (mode != DUOLM_MODE_MIS && mode != DUOLM_MODE_INDEPENDENT) return fail(DUOLM_EINVAL, "bad mode");
+  if (layer < 0 || layer > R->dims.n_layers || stage < 0 || stage > DUOLM_STAGE_EMBED)
+    return fail(DUOLM_EINVAL, "bad layer/stage");
+  if (layer == R->dims.n_layers && stage != DUOLM_STAGE_LAYER_OUT) return fail(DUOLM_EINVAL, "bad stage");
+  if (stage == DUOLM_STAGE_EMBED && layer != 0) return fail(DUOLM_EINVAL, "embed stage is layer 0 only");
+  std::vector<int32_t> L, K, ids;
+  int rc = flatten_requests(reqs, n_req, L, K, ids);
+  if (rc) return rc;
+  CallInput in{L.data(), K.data(), n_req};
+  int64_t total_ids = 0, total_scores = 0;
+  if ((rc = validate_lengths(R, in, total_ids, total_scores))) return rc;
+  const int64_t lim = (int64_t)R->dims.vocab + R->n_vid;
+  for (int32_t id : ids)
+    if (id < 0 || id >= lim) return fail(DUOLM_ERANGE, "id %d outside [0, %lld)", id, (long long)lim);
+  std::vector<Plan> plans;
+  build_plans(R, in, mode, plans);
+  if (plans.size() != 1) return fail(DUOLM_EINVAL, "debug batch must fit one launch");
+  const Plan& P = plans[0];
+  const auto& D = R->dims;
+  size_t row_bytes = 0;
+  const int buf_stage = layer == D.n_layers ? DUOLM_STAGE_LAYER_OUT : stage;
+  switch (buf_stage) {
+    case DUOLM_STAGE_ATTN_NORM: case DUOLM_STAGE_MLP_NORM: row_bytes = (size_t)D.d_model * 2; break;
+    case DUOLM_STAGE_QKV: case DUOLM_STAGE_QK_ROPE: row_bytes = (size_t)R->nqkv * 2; break;
+    case DUOLM_STAGE_ATTN: row_bytes = (size_t)D.n_heads * D.head_dim * 2; break;
+    case DUOLM_STAGE_SWIGLU: row_bytes = (size_t)D.d_ffn * 2; break;
+    default: row_bytes = (size_t)D.d_model * 4;
+  }
+  if (nbytes != row_bytes * P.T) return fail(DUOLM_EINVAL, "nbytes %llu != %zu", (unsigned long long)nbytes, row_bytes * P.T);
+  HIP_TRY(hipSetDevice(R->device));
+  if ((rc = ensure_rows(R, P.T))) return rc;
+  if ((rc = ensure_meta(R, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size())))
+    return rc;
+  if ((rc = ensure_buf(R->d_ids, R->cap_ids, total_ids, R->stream))) return rc;
+  if ((rc = ensure_buf(R->d_out, R->cap_out, total_scores, R->stream))) return rc;
+  hipStream_t s = R->stream;
+  HIP_TRY(hipMemcpyAsync(R->d_ids, ids.data(), ids.size() * 4, hipMemcpyHostToDevice, s));
+  *R->h_err = 0;
+  HIP_TRY(hipMemcpyAsync(R->d_err, R->h_err, 4, hipMemcpyHostToDevice, s));
+  if ((rc = upload_plan(R, P, s))) return rc;
+  Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size()};
+  Enq q{R, s, nullptr, nullptr};
+  q.stop_layer = layer == D.n_layers ? D.n_layers - 1 : layer;
+  q.stop_stage = buf_stage;
+  enqueue_forward(q, c);
+  HIP_TRY(hipGetLastError());
+  const void* src = nullptr;
+  switch (buf_stage) {
+    case DUOLM_STAGE_ATTN_NORM: case DUOLM_STAGE_MLP_NORM: src = R->Xn; break;
+    case DUOLM_STAGE_QKV: case DUOLM_STAGE_QK_ROPE: src = R->QKV; break;
+    case DUOLM_STAGE_ATTN: src = R->Ob; break;
+    case DUOLM_STAGE_SWIGLU: src = R->Hb; break;
+    default: src = R->X;
+  }
+  HIP_TRY(hipMemcpyAsync(host_out, src, nbytes, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return DUOLM_OK;
+}
+
+int duolm_debug_gemm(int32_t epi, const uint16_t* A, const uint16_t* W, void* C, int32_t M, int32_t N, int32_t K,
+                     void* stream) {
+  if (!A || !W || !C) return fail(DUOLM_EINVAL, "NULL argument");
+  if (epi < 0 || epi > 2 || M < 1) return fail(DUOLM_EINVAL, "bad epilogue or M");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* dM = nullptr;
+  HIP_TRY(hipMalloc((void**)&dM, 4));
+  hipError_t e = hipMemcpyAsync(dM, &M, 4, hipMemcpyHostToDevice, s);
+  const int ldc = epi == EPI_SWIGLU ? N / 2 : N;
+  bool ok = e == hipSuccess && launch_gemm(s, epi, M, A, K, W, K, C, ldc, dM, N, K);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(dM);
+  if (e != hipSuccess) return fail(DUOLM_EHIP, "gemm: %s", hipGetErrorString(e));
+  if (!ok) return fail(DUOLM_EINVAL, "unsupported GEMM shape N=%d K=%d", N, K);
+  return DUOLM_OK;
+}
+
+int duolm_copy_device(void* dst, const void* src, uint64_t nbytes, void* stream) {
+  if (!dst || !src || nbytes % 16) return fail(DUOLM_EINVAL, "bad copy arguments");
+  launch_copy((hipStream_t)stream, dst, src, nbytes);
+  HIP_TRY(hipGetLastError());
+  return DUOLM_OK;
+}
+
+}  // extern "C"

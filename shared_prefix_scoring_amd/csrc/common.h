@@ -1,0 +1,83 @@
+// Shared definitions of the DuoLM MIS ranker library: the per-call batch
+// descriptors that the host planner writes and the kernels read, and small
+// device helpers.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace duolm {
+
+// ---------------------------------------------------------------------------
+// Batch description, uploaded once per forward launch.
+//
+// Rows of the activation buffers are packed sequence by sequence.  A sequence
+// has L causal rows (positions 0..L-1) followed by K one-row candidate
+// branches (all at position L).  MIS: one sequence per request.  Independent
+// scoring: one sequence per (request, candidate) with L = prefix + 1, K = 0.
+// Row rho of a sequence takes its id from ids[id_off + rho] when rho < id_len,
+// else from ids[cand_id_off + rho - id_len].
+// ---------------------------------------------------------------------------
+struct SeqDesc {
+  int32_t row_off;
+  int32_t L;
+  int32_t K;
+  int32_t id_off;
+  int32_t id_len;
+  int32_t cand_id_off;
+  int32_t pad0, pad1;
+};
+
+// A tile of query rows: prefix tiles start at row r0 of the sequence,
+// branch tiles at candidate r0.
+struct WorkItem {
+  int32_t seq;
+  int32_t r0;
+};
+
+struct CallHeader {
+  int32_t T;         // rows in this launch
+  int32_t n_seq;
+  int32_t n_pitems;  // prefix attention tiles
+  int32_t n_bitems;  // branch attention tiles
+  int32_t n_scores;  // rows read by the score head
+  int32_t score_off; // index of this launch's first score in the call's output
+  int32_t pad[10];
+};
+static_assert(sizeof(CallHeader) == 64, "header layout");
+
+constexpr int kMaxPos = 32768;  // rotary table length; prefixes are shorter
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// round-to-nearest-even fp32 -> bf16 (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, h);
+  return (float)v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+}  // namespace duolm

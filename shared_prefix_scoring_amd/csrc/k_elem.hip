@@ -1,0 +1,196 @@
+// Row-wise kernels of the ranker forward: VID-aware embedding gather,
+// RMSNorm, per-head q/k RMSNorm + rotary embedding, and the score head.
+// All are HBM-bound streaming kernels: one 64-lane wave per row (or per
+// (row, head) group), 16-byte vector accesses, fp32 arithmetic.
+#include "launch.h"
+
+namespace duolm {
+
+// ---------------------------------------------------------------------------
+// Embedding gather over the extended vocabulary [0, V + N): ids below V read
+// the bf16 token embedding, ids V + iota read row iota of the fp16 item table
+// ("DuoLM: Fast and Effective Personalized Recommendation with Language
+// Models", 方法步骤详情 step 3).  Both widen exactly to the fp32 residual
+// stream.  Also writes each row's logical position: causal row rho -> rho,
+// every candidate row -> L (same page, 核心方法 / step 4).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, DevBatch b,
+                                               const uint16_t* __restrict__ E,
+                                               const uint16_t* __restrict__ D, int V, int64_t n_vid,
+                                               int d, float* __restrict__ X, int32_t* __restrict__ pos) {
+  const int T = b.hdr->T;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= T) return;
+  // sequence holding this row: last s with seq_row_off[s] <= row
+  int lo = 0, hi = b.hdr->n_seq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (b.seq_row_off[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const SeqDesc sd = b.seqs[lo];
+  const int rho = row - sd.row_off;
+  const int id = rho < sd.id_len ? ids[sd.id_off + rho] : ids[sd.cand_id_off + (rho - sd.id_len)];
+  if (lane == 0) pos[row] = rho < sd.L ? rho : sd.L;
+  float* xr = X + (size_t)row * d;
+  const int nchunk = d >> 3;  // 8 values per chunk
+  if (id < 0 || (int64_t)id >= (int64_t)V + n_vid) {
+    if (lane == 0) atomicOr(b.err, 1);
+    for (int c = lane; c < nchunk; c += 64) {
+      reinterpret_cast<float4*>(xr + c * 8)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      reinterpret_cast<float4*>(xr + c * 8)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  const bool tok = id < V;
+  const uint16_t* src = tok ? E + (size_t)id * d : D + (size_t)(id - V) * d;
+  for (int c = lane; c < nchunk; c += 64) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + c * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t lo16 = (uint16_t)(w[e] & 0xffffu), hi16 = (uint16_t)(w[e] >> 16);
+      f[2 * e] = tok ? bf16_to_f32(lo16) : f16_to_f32(lo16);
+      f[2 * e + 1] = tok ? bf16_to_f32(hi16) : f16_to_f32(hi16);
+    }
+    reinterpret_cast<float4*>(xr + c * 8)[0] = make_float4(f[0], f[1], f[2], f[3]);
+    reinterpret_cast<float4*>(xr + c * 8)[1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+}
+
+void launch_embed(hipStream_t s, int cap_rows, const int32_t* ids, DevBatch b, const uint16_t* E,
+                  const uint16_t* D, int V, int64_t n_vid, int d, float* X, int32_t* pos) {
+  if (cap_rows <= 0) return;
+  hipLaunchKernelGGL(k_embed, dim3((cap_rows + 3) / 4), dim3(256), 0, s, ids, b, E, D, V, n_vid, d, X, pos);
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, fp32 math, bf16 out.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ X, const float* __restrict__ g,
+                                                 uint16_t* __restrict__ Y, const CallHeader* __restrict__ hdr,
+                                                 int d, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= hdr->T) return;
+  const float* xr = X + (size_t)row * d;
+  const int nq = d >> 2;
+  float ss = 0.f;
+  for (int c = lane; c < nq; c += 64) {
+    const float4 v = reinterpret_cast<const float4*>(xr)[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  uint16_t* yr = Y + (size_t)row * d;
+  for (int c = lane; c < nq; c += 64) {
+    const float4 v = reinterpret_cast<const float4*>(xr)[c];
+    const float4 gg = reinterpret_cast<const float4*>(g)[c];
+    uint2 o;
+    o.x = pack_bf16x2(v.x * inv * gg.x, v.y * inv * gg.y);
+    o.y = pack_bf16x2(v.z * inv * gg.z, v.w * inv * gg.w);
+    reinterpret_cast<uint2*>(yr)[c] = o;
+  }
+}
+
+void launch_rmsnorm(hipStream_t s, int cap_rows, const float* X, const float* g, uint16_t* Y,
+                    const CallHeader* hdr, int d, float eps) {
+  if (cap_rows <= 0) return;
+  hipLaunchKernelGGL(k_rmsnorm, dim3((cap_rows + 3) / 4), dim3(256), 0, s, X, g, Y, hdr, d, eps);
+}
+
+// ---------------------------------------------------------------------------
+// Per-head RMSNorm of q and k (gain over head_dim) followed by the rotary
+// embedding at each row's logical position, in place on the bf16 q|k|v row.
+// Rotate-half layout: pair (i, i + hd/2) turns by pos * base^(-2i/hd); the
+// cos/sin table is built on the host in double precision.  One thread per
+// pair; the hd/2 threads of a head reduce with shuffles inside their group.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_qk_rope(uint16_t* __restrict__ QKV, int ld,
+                                                 const CallHeader* __restrict__ hdr,
+                                                 const int32_t* __restrict__ pos,
+                                                 const float* __restrict__ gq, const float* __restrict__ gk,
+                                                 const float2* __restrict__ rope, int H, int Hkv, int hd,
+                                                 float eps) {
+  const int half = hd >> 1;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int i = idx % half;
+  const int rh = idx / half;
+  const int nh = H + Hkv;
+  const int head = rh % nh;
+  const int row = rh / nh;
+  if (row >= hdr->T) return;  // uniform across the head's group (half divides 64)
+  const bool isq = head < H;
+  const int col = isq ? head * hd : H * hd + (head - H) * hd;
+  const float* g = isq ? gq : gk;
+  uint16_t* p = QKV + (size_t)row * ld + col;
+  const float x1 = bf16_to_f32(p[i]);
+  const float x2 = bf16_to_f32(p[i + half]);
+  float ss = x1 * x1 + x2 * x2;
+  for (int m = half >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, half);
+  const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
+  const float y1 = x1 * inv * g[i];
+  const float y2 = x2 * inv * g[i + half];
+  const float2 cs = rope[(size_t)pos[row] * half + i];
+  p[i] = f32_to_bf16(y1 * cs.x - y2 * cs.y);
+  p[i + half] = f32_to_bf16(y2 * cs.x + y1 * cs.y);
+}
+
+void launch_qk_rope(hipStream_t s, int cap_rows, uint16_t* QKV, int ld, const CallHeader* hdr,
+                    const int32_t* pos, const float* gq, const float* gk, const float2* rope, int H,
+                    int Hkv, int hd, float eps) {
+  if (cap_rows <= 0) return;
+  const long threads = (long)cap_rows * (H + Hkv) * (hd / 2);
+  hipLaunchKernelGGL(k_qk_rope, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, QKV, ld, hdr,
+                     pos, gq, gk, rope, H, Hkv, hd, eps);
+}
+
+// ---------------------------------------------------------------------------
+// Score head: s = w . RMSNorm_final(x) on the listed rows, fp32 throughout
+// (shared linear head, "DuoLM: Fast and Effective Personalized Recommendation
+// with Language Models", 核心方法).  Writes nothing when the gather flagged an
+// out-of-range id.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_head(const float* __restrict__ X, DevBatch b,
+                                              const float* __restrict__ gf, const float* __restrict__ w,
+                                              float* __restrict__ scores, int d, float eps) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= b.hdr->n_scores || *b.err) return;
+  const float* xr = X + (size_t)b.head_rows[i] * d;
+  float ss = 0.f, dot = 0.f;
+  for (int c = lane; c < (d >> 2); c += 64) {
+    const float4 v = reinterpret_cast<const float4*>(xr)[c];
+    const float4 gg = reinterpret_cast<const float4*>(gf)[c];
+    const float4 ww = reinterpret_cast<const float4*>(w)[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    dot += v.x * gg.x * ww.x + v.y * gg.y * ww.y + v.z * gg.z * ww.z + v.w * gg.w * ww.w;
+  }
+  ss = wave_sum(ss);
+  dot = wave_sum(dot);
+  if (lane == 0) scores[b.hdr->score_off + i] = dot / sqrtf(ss / (float)d + eps);
+}
+
+void launch_head(hipStream_t s, int cap_scores, const float* X, DevBatch b, const float* gf,
+                 const float* w, float* scores, int d, float eps) {
+  if (cap_scores <= 0) return;
+  hipLaunchKernelGGL(k_head, dim3((cap_scores + 3) / 4), dim3(256), 0, s, X, b, gf, w, scores, d, eps);
+}
+
+// ---------------------------------------------------------------------------
+// Plain 16-byte copy (grid-stride), used to calibrate byte counters.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_copy(uint4* __restrict__ dst, const uint4* __restrict__ src, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = src[i];
+}
+
+void launch_copy(hipStream_t s, void* dst, const void* src, size_t nbytes) {
+  const size_t n = nbytes / 16;
+  if (n == 0) return;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)dst, (const uint4*)src, n);
+}
+
+}  // namespace duolm

@@ -1,0 +1,48 @@
+// Host-side launchers of the HIP kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace duolm {
+
+// Device views of one launch's batch description.
+struct DevBatch {
+  const CallHeader* hdr;
+  const int32_t* seq_row_off;  // [n_seq + 1] first row of each sequence, then T
+  const SeqDesc* seqs;
+  const WorkItem* pitems;
+  const WorkItem* bitems;
+  const int32_t* head_rows;
+  int32_t* err;  // call-wide flag: nonzero after an out-of-range id
+};
+
+// Grids are sized from host upper bounds ("cap" arguments); every kernel reads
+// the true counts from the CallHeader and idles the surplus, so one captured
+// graph serves any batch up to its caps.
+void launch_embed(hipStream_t s, int cap_rows, const int32_t* ids, DevBatch b, const uint16_t* E,
+                  const uint16_t* D, int V, int64_t n_vid, int d, float* X, int32_t* pos);
+void launch_rmsnorm(hipStream_t s, int cap_rows, const float* X, const float* g, uint16_t* Y,
+                    const CallHeader* hdr, int d, float eps);
+void launch_qk_rope(hipStream_t s, int cap_rows, uint16_t* QKV, int ld, const CallHeader* hdr,
+                    const int32_t* pos, const float* gq, const float* gk, const float2* rope, int H,
+                    int Hkv, int hd, float eps);
+void launch_head(hipStream_t s, int cap_scores, const float* X, DevBatch b, const float* gf,
+                 const float* w, float* scores, int d, float eps);
+void launch_copy(hipStream_t s, void* dst, const void* src, size_t nbytes);
+
+// GEMM epilogues
+enum { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+// C = epi(A[M,K] W[N,K]^T); M read from *dM (<= cap_m).  Returns false if the
+// shape is unsupported (N % 64 or K % 64 nonzero).
+bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W,
+                 int ldw, void* C, int ldc, const int32_t* dM, int N, int K);
+
+// Attention over one launch's work items.  Returns rows covered per item.
+int attn_rows_per_item(bool branch, int group);
+bool attn_supported(int head_dim);
+void launch_attn(hipStream_t s, bool branch, int hd, int cap_items, const uint16_t* QKV, int ld,
+                 uint16_t* O, int ldo, DevBatch b, int H, int Hkv, float scale_log2);
+
+}  // namespace duolm

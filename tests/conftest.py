@@ -43,3 +43,33 @@ def qwen():
     w = synth.make_weights(cfg, seed=0)
     D = synth.make_vid_table(cfg, w)
     return cfg, w, D, OracleModel.from_arrays(cfg, w, D)
+
+
+@pytest.fixture(scope="session")
+def gpu_tiny(tiny):
+    import shared_prefix_scoring_amd as spa
+    cfg, w, D, model = tiny
+    r = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
+    r.load_vid_table(D)
+    yield cfg, w, D, model, r
+    r.close()
+
+
+@pytest.fixture(scope="session")
+def gpu_tiny_gains(tiny_gains):
+    import shared_prefix_scoring_amd as spa
+    cfg, w, D, model = tiny_gains
+    r = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
+    r.load_vid_table(D)
+    yield cfg, w, D, model, r
+    r.close()
+
+
+@pytest.fixture(scope="session")
+def gpu_qwen(qwen):
+    import shared_prefix_scoring_amd as spa
+    cfg, w, D, model = qwen
+    r = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
+    r.load_vid_table(D)
+    yield cfg, w, D, model, r
+    r.close()

@@ -1,0 +1,206 @@
+"""End-to-end parity of the GPU MIS forward with the float64 oracle, at the
+workload shapes: tiny (L=48, K=8), one 0.6B request (L=452, K=100), a packed
+64-request varlen batch (sampled requests checked against the oracle), the
+K=8 rating mix, and the L=4096 / K=512 stress shape (checked against GPU
+independent scoring on sampled candidates).  Also: GPU MIS versus GPU
+independent scoring, graph replay versus eager launch, determinism, batch
+and permutation invariance, and the error paths."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import oracle_mis
+import shared_prefix_scoring_amd as spa
+from parity import MIS_VS_IND_TOL, SCORE_TOL, score_err, top10_check
+
+pytestmark = pytest.mark.gpu
+
+IND = spa.DUOLM_MODE_INDEPENDENT
+
+
+def reqs_of(cfg, cid, n=None, **kw):
+    return [(r.prefix, r.cands) for r in synth.make_requests(cid, cfg, n_requests=n, **kw)]
+
+
+def split(scores, reqs):
+    out, o = [], 0
+    for _, c in reqs:
+        out.append(scores[o:o + len(c)])
+        o += len(c)
+    return out
+
+
+def check_against_oracle(model, reqs, gpu_scores, which=None):
+    per = split(gpu_scores, reqs)
+    errs, swaps = [], 0
+    for i in (range(len(reqs)) if which is None else which):
+        p, c = reqs[i]
+        ref = oracle_mis(model, p, c)
+        e = score_err(per[i], ref)
+        errs.append(e)
+        ok, s = top10_check(per[i], ref)
+        swaps += s
+        assert e <= SCORE_TOL, (i, e)
+        assert ok, i
+    print(f"max rel score err {max(errs):.3e}, requests with strict top-10 swaps: {swaps}")
+    return max(errs)
+
+
+@pytest.mark.parametrize("fixture", ["gpu_tiny", "gpu_tiny_gains"])
+def test_tiny_workload(fixture, request):
+    cfg, _, _, model, r = request.getfixturevalue(fixture)
+    reqs = reqs_of(cfg, 1)
+    for g in (False, True):
+        check_against_oracle(model, reqs, r.score(reqs, use_graph=g))
+
+
+def test_tiny_many_shapes(gpu_tiny):
+    # ragged prefixes and candidate counts across tile boundaries, K up to 300
+    cfg, _, _, model, r = gpu_tiny
+    rng = np.random.default_rng(11)
+    reqs = []
+    for L, K in [(1, 1), (2, 3), (63, 1), (64, 129), (65, 128), (130, 7), (200, 300)]:
+        reqs.append((rng.integers(0, cfg.vocab + cfg.n_vid, L).astype(np.int32),
+                     (cfg.vocab + rng.choice(cfg.n_vid, K, replace=K > cfg.n_vid)).astype(np.int32)))
+    check_against_oracle(model, reqs, r.score(reqs))
+
+
+def test_qwen_single_request(gpu_qwen):
+    cfg, _, _, model, r = gpu_qwen
+    reqs = reqs_of(cfg, 2)
+    assert len(reqs[0][0]) == 452 and len(reqs[0][1]) == 100
+    check_against_oracle(model, reqs, r.score(reqs))
+
+
+def test_qwen_c64_batch_sampled(gpu_qwen):
+    cfg, _, _, model, r = gpu_qwen
+    reqs = reqs_of(cfg, 3, n=64)
+    s = r.score(reqs)
+    assert s.shape[0] == 6400 and np.all(np.isfinite(s))
+    lens = [len(p) for p, _ in reqs]
+    which = [int(np.argmin(lens)), int(np.argmax(lens)), 17]
+    check_against_oracle(model, reqs, s, which=which)
+    # sampled requests scored alone give bit-identical scores (batch invariance)
+    per = split(s, reqs)
+    for i in which:
+        np.testing.assert_array_equal(r.score([reqs[i]]), per[i])
+
+
+def test_qwen_rating_mix(gpu_qwen):
+    cfg, _, _, model, r = gpu_qwen
+    reqs = reqs_of(cfg, 4, n=8)
+    for g in (False, True):
+        check_against_oracle(model, reqs, r.score(reqs, use_graph=g))
+
+
+def test_mis_vs_independent_qwen(gpu_qwen):
+    cfg, _, _, model, r = gpu_qwen
+    reqs = reqs_of(cfg, 2)
+    mis = r.score(reqs)
+    ind = r.score(reqs, mode=IND)
+    e = score_err(mis, ind)
+    print(f"GPU MIS vs GPU independent: max rel diff {e:.3e}")
+    assert e <= MIS_VS_IND_TOL
+
+
+def test_stress_shape_sampled(gpu_qwen):
+    # L = 4096, K = 512: MIS against independent scoring of sampled candidates
+    cfg, _, _, model, r = gpu_qwen
+    (p, c), = reqs_of(cfg, 5, n=1)
+    assert len(p) == 4096 and len(c) == 512
+    mis = r.score([(p, c)])
+    pick = [0, 131, 300, 511]
+    ind = r.score([(p, c[pick])], mode=IND)
+    e = score_err(mis[pick], ind)
+    print(f"stress shape: MIS vs independent on {len(pick)} candidates: {e:.3e}")
+    assert e <= MIS_VS_IND_TOL
+    # the candidate subset scored by MIS alone matches the full-K scores bit for bit
+    np.testing.assert_array_equal(r.score([(p, c[pick])]), mis[pick])
+
+
+def test_graph_matches_eager_and_repeats(gpu_qwen):
+    cfg, _, _, _, r = gpu_qwen
+    reqs = reqs_of(cfg, 3, n=12)
+    eager = r.score(reqs, use_graph=False)
+    for _ in range(3):
+        np.testing.assert_array_equal(r.score(reqs, use_graph=True), eager)
+    # a different batch between replays of the same bucket
+    other = reqs_of(cfg, 3, n=12, seed=99)
+    r.score(other, use_graph=True)
+    np.testing.assert_array_equal(r.score(reqs, use_graph=True), eager)
+
+
+def test_permutation_and_leakage(gpu_tiny):
+    cfg, _, _, _, r = gpu_tiny
+    (p, c), = reqs_of(cfg, 1)
+    base = r.score([(p, c)])
+    perm = np.random.default_rng(3).permutation(len(c))
+    np.testing.assert_array_equal(r.score([(p, c[perm])]), base[perm])
+    c2 = c.copy()
+    c2[2] = cfg.vocab + (int(c[2]) - cfg.vocab + 1) % cfg.n_vid
+    other = r.score([(p, c2)])
+    keep = np.arange(len(c)) != 2
+    np.testing.assert_array_equal(other[keep], base[keep])
+
+
+def test_device_entry_point(gpu_qwen):
+    cfg, _, _, _, r = gpu_qwen
+    reqs = reqs_of(cfg, 3, n=5)
+    ids, L, K = synth.pack_ids([synth.Request(np.asarray(p), np.asarray(c)) for p, c in reqs])
+    d_ids = torch.from_numpy(ids).cuda()
+    d_s = torch.full((int(K.sum()),), -7.0, device="cuda")
+    r.score_dev(L, K, d_ids.data_ptr(), d_s.data_ptr())
+    np.testing.assert_array_equal(d_s.cpu().numpy(), r.score(reqs))
+    # an out-of-range id: ERANGE and the output left untouched
+    bad = ids.copy()
+    bad[3] = cfg.vocab + cfg.n_vid
+    d_bad = torch.from_numpy(bad).cuda()
+    d_s2 = torch.full((int(K.sum()),), -7.0, device="cuda")
+    with pytest.raises(spa.DuolmError) as e:
+        r.score_dev(L, K, d_bad.data_ptr(), d_s2.data_ptr())
+    assert e.value.status == "ERANGE"
+    assert torch.all(d_s2 == -7.0)
+
+
+def test_host_errors(gpu_tiny):
+    cfg, _, _, _, r = gpu_tiny
+    p = np.arange(5, dtype=np.int32)
+    with pytest.raises(spa.DuolmError) as e:
+        r.score([(p, np.array([cfg.vocab + cfg.n_vid], np.int32))])
+    assert e.value.status == "ERANGE"
+    with pytest.raises(spa.DuolmError) as e:
+        r.score([(p, np.array([-1], np.int32))])
+    assert e.value.status == "ERANGE"
+    with pytest.raises(spa.DuolmError) as e:
+        r.score([(p, np.array([], np.int32))])
+    assert e.value.status == "EINVAL"
+    with pytest.raises(spa.DuolmError) as e:
+        r.score([(np.array([], np.int32), np.array([cfg.vocab], np.int32))])
+    assert e.value.status == "EINVAL"
+
+
+def test_no_table_is_estate(tiny):
+    cfg, w, _, _ = tiny
+    r = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
+    try:
+        with pytest.raises(spa.DuolmError) as e:
+            r.score([(np.arange(4, dtype=np.int32), np.array([cfg.vocab], np.int32))])
+        assert e.value.status == "ESTATE"
+        s = r.score([(np.arange(4, dtype=np.int32), np.array([7, 8], np.int32))])  # text-only ids work
+        assert np.all(np.isfinite(s))
+    finally:
+        r.close()
+
+
+def test_profiling_counters(gpu_qwen):
+    cfg, _, _, _, r = gpu_qwen
+    reqs = reqs_of(cfg, 3, n=16)
+    r.set_profiling(["gemm_gateup", "attn_branch"])
+    for g in (False, True):
+        r.score(reqs, use_graph=g)
+    st = r.kernel_stats("gemm_gateup")
+    assert st.launches == 2 * cfg.n_layers and st.total_ms > 0 and st.flops > 0
+    assert r.kernel_stats("attn_branch").launches == 2 * cfg.n_layers
+    assert r.kernel_stats("gemm_qkv").launches == 0
+    r.set_profiling([])
