@@ -6,17 +6,26 @@
 // Design (gfx950 / CDNA4):
 //   * block tile BM x BN x 64, WM x WN waves, each wave owning a
 //     (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks accumulated in fp32;
-//   * operands staged global -> registers -> LDS, two LDS stages so the next
-//     k-slab's global loads are in flight while the current one is multiplied;
-//     one barrier per k-slab;
+//     the large shape is 256 x 256 with 8 waves (two per SIMD, 64 x 128
+//     each), so one wave's LDS and barrier waits overlap the other's MFMAs;
+//   * operands go global -> LDS directly with global_load_lds_dwordx4 (one
+//     instruction fills 1 KB of LDS = 8 rows of 128 bytes, lane i writing
+//     bytes [16i, 16i+16)); no staging registers, so the accumulators can
+//     fill the AGPR file and the loads of k-slab kt+1 fly while slab kt is
+//     multiplied out of the other LDS stage;
 //   * LDS rows are 128 bytes (64 bf16); the 16-byte chunk index is XOR-swizzled
-//     with (row >> 1) & 7 so the 16 lanes of a ds_read_b128 phase hit 64
-//     distinct banks;
+//     with (row ^ (row >> 3)) & 7 -- each lane fetches the global chunk that
+//     belongs at its LDS slot -- so the 32 rows of a fragment read hit
+//     distinct bank groups;
+//   * fragments are double-buffered in registers: the ds_read_b128s of k-step
+//     ks+1 are issued before the MFMAs of k-step ks;
 //   * the k loop order is fixed and there is no split-K, so every output row
 //     is computed by the same instruction sequence whatever M is or where the
 //     row sits: results are batch invariant;
 //   * epilogues: bf16 store (QKV), fp32 residual add (O-proj, down-proj),
 //     SwiGLU on interleaved gate/up column blocks (gate/up projection).
+#include <type_traits>
+
 #include "launch.h"
 
 namespace duolm {
@@ -25,22 +34,32 @@ namespace {
 
 constexpr int BK = 64;
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 
-template <int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// 16 bytes per lane, global -> LDS; lane i lands at lds + 16 i
+__device__ __forceinline__ void load_lds16(const uint16_t* g, lds_u16_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int BM, int BN, int WM, int WN, int EPI, bool SCHED>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restrict__ A, int lda,
                                                       const uint16_t* __restrict__ W, int ldw,
                                                       void* __restrict__ Cv, int ldc,
                                                       const int32_t* __restrict__ dM, int N, int K) {
-  constexpr int NT = WM * WN * 64;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NI = WTN / 32;
-  constexpr int A_PER_T = BM * BK / 8 / NT;
-  constexpr int B_PER_T = BN * BK / 8 / NT;
-  static_assert(A_PER_T * NT * 8 == BM * BK && B_PER_T * NT * 8 == BN * BK, "tile/thread mismatch");
+  constexpr int GA = BM / 8 / NW, GB = BN / 8 / NW;  // 8-row groups each wave loads
+  constexpr int STAGE = (BM + BN) * BK;               // elements per LDS stage
+  static_assert(GA * NW * 8 == BM && GB * NW * 8 == BN, "tile/wave mismatch");
   static_assert(EPI != EPI_SWIGLU || NI % 2 == 0, "swiglu needs gate/up block pairs");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][(BM + BN) * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
 
   const int M = *dM;
   const int n_tiles = N / BN;
@@ -49,39 +68,63 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   if (m0 >= M) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
-
-  // global -> register staging
-  uint4 ra[A_PER_T], rb[B_PER_T];
-  const uint16_t* a_ptr[A_PER_T];
-  const uint16_t* b_ptr[B_PER_T];
-  int a_lds[A_PER_T], b_lds[B_PER_T];
-#pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int c = tid + i * NT;
-    const int r = c >> 3, kc = c & 7;
-    const int gr = min(m0 + r, M - 1);  // rows past M load a valid row; never stored
-    a_ptr[i] = A + (size_t)gr * lda + kc * 8;
-    a_lds[i] = r * BK + ((kc ^ swz(r)) << 3);
-  }
-#pragma unroll
-  for (int i = 0; i < B_PER_T; ++i) {
-    const int c = tid + i * NT;
-    const int r = c >> 3, kc = c & 7;
-    b_ptr[i] = W + (size_t)(n0 + r) * ldw + kc * 8;
-    b_lds[i] = BM * BK + r * BK + ((kc ^ swz(r)) << 3);
-  }
-
-  // per-lane LDS fragment offsets (in elements) for k-step 0
-  int a_frag[MI], b_frag[NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) a_frag[mi] = (wm * WTM + mi * 32 + (lane & 31)) * BK;
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni) b_frag[ni] = BM * BK + (wn * WTN + ni * 32 + (lane & 31)) * BK;
   const int half = lane >> 5;
+
+  // per-lane source of this wave's row groups: row g*8 + lane/8, the chunk
+  // whose swizzled slot is lane%8
+  const uint16_t* pa[GA];
+  const uint16_t* pb[GB];
+#pragma unroll
+  for (int j = 0; j < GA; ++j) {
+    const int r = (wave + NW * j) * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ swz(r);
+    pa[j] = A + (size_t)min(m0 + r, M - 1) * lda + kc * 8;  // rows past M load a valid row, never stored
+  }
+#pragma unroll
+  for (int j = 0; j < GB; ++j) {
+    const int r = (wave + NW * j) * 8 + (lane >> 3);
+    const int kc = (lane & 7) ^ swz(r);
+    pb[j] = W + (size_t)(n0 + r) * ldw + kc * 8;
+  }
+  lds_u16_t* lds = (lds_u16_t*)(lds_void_t*)smem;
+
+  auto issue = [&](int kt, int st) {
+#pragma unroll
+    for (int j = 0; j < GA; ++j)
+      load_lds16(pa[j] + kt * BK, lds + st * STAGE + (wave + NW * j) * 8 * BK);
+#pragma unroll
+    for (int j = 0; j < GB; ++j)
+      load_lds16(pb[j] + kt * BK, lds + st * STAGE + BM * BK + (wave + NW * j) * 8 * BK);
+  };
+
+  // fragment rows and their swizzles
+  int a_row[MI], a_sw[MI], b_row[NI], b_sw[NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int r = wm * WTM + mi * 32 + (lane & 31);
+    a_row[mi] = r * BK;
+    a_sw[mi] = swz(r);
+  }
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    const int r = wn * WTN + ni * 32 + (lane & 31);
+    b_row[ni] = BM * BK + r * BK;
+    b_sw[ni] = swz(r);
+  }
+
+  bf16x8_t fa[2][MI], fb[2][NI];
+  auto read_frags = [&](int st, int ks, int buf) {
+    const int kc = ks * 2 + half;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      fa[buf][mi] = *reinterpret_cast<const bf16x8_t*>(&smem[st * STAGE + a_row[mi] + ((kc ^ a_sw[mi]) << 3)]);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+      fb[buf][ni] = *reinterpret_cast<const bf16x8_t*>(&smem[st * STAGE + b_row[ni] + ((kc ^ b_sw[ni]) << 3)]);
+  };
 
   f32x16_t acc[MI][NI];
 #pragma unroll
@@ -91,50 +134,72 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  auto load_global = [&](int kt) {
+  auto mfma_step = [&](int buf, int from, int to) {  // MFMAs number from..to-1 of one k-step
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_ptr[i] + kt * BK);
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_ptr[i] + kt * BK);
+    for (int i = from; i < to; ++i)
+      acc[i / NI][i % NI] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i / NI], fb[buf][i % NI], acc[i / NI][i % NI], 0, 0, 0);
   };
-  auto store_lds = [&](int st) {
+
+  // One k-slab.  Program order, pinned with scheduling-group barriers:
+  //   k-steps 0..2: MFMAs of step ks interleaved with the fragment reads of
+  //   step ks+1 and with the global->LDS loads of the next slab;
+  //   k-step 3: half of its MFMAs, then the slab barrier, then the first
+  //   fragment reads of the next slab, then the other half -- so the barrier
+  //   and the LDS latency hide behind matrix work.
+  constexpr int NM = MI * NI;          // MFMAs per k-step
+  constexpr int NR = MI + NI;          // fragment reads per k-step
+  constexpr int NG = GA + GB;          // global->LDS loads per slab
+  auto slab = [&](int kt, auto has_next) {
+    constexpr bool NEXT = decltype(has_next)::value;
+    const int st = kt & 1;
+    if constexpr (NEXT) issue(kt + 1, st ^ 1);
+    read_frags(st, 1, 1);
+    mfma_step(0, 0, NM);
+    read_frags(st, 2, 0);
+    mfma_step(1, 0, NM);
+    read_frags(st, 3, 1);
+    mfma_step(0, 0, NM);
+    mfma_step(1, 0, NM / 2);
+    // pipeline order of the region above
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) *reinterpret_cast<uint4*>(&smem[st][a_lds[i]]) = ra[i];
+    for (int ks = 0; ks < (SCHED ? 3 : 0); ++ks) {
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) *reinterpret_cast<uint4*>(&smem[st][b_lds[i]]) = rb[i];
+      for (int i = 0; i < NR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      if constexpr (NEXT) {
+#pragma unroll
+        for (int i = 0; i < (NG + 2) / 3; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    }
+    if constexpr (SCHED) __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
+    wait_loads();
+    __syncthreads();
+    if constexpr (NEXT) read_frags(st ^ 1, 0, 0);
+    mfma_step(1, NM / 2, NM);
+    if constexpr (NEXT && SCHED) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      }
+    }
+    if constexpr (SCHED) __builtin_amdgcn_sched_group_barrier(0x008, NM, 1);
   };
 
   const int KT = K / BK;
-  load_global(0);
-  store_lds(0);
+  issue(0, 0);
+  wait_loads();
   __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < KT) load_global(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kc = ks * 2 + half;
-      bf16x8_t af[MI], bfr[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int r = wm * WTM + mi * 32 + (lane & 31);
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(&smem[st][a_frag[mi] + ((kc ^ swz(r)) << 3)]);
-      }
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int r = wn * WTN + ni * 32 + (lane & 31);
-        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(&smem[st][b_frag[ni] + ((kc ^ swz(r)) << 3)]);
-      }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (kt + 1 < KT) store_lds(st ^ 1);
-    __syncthreads();
-  }
+  read_frags(0, 0, 0);
+  for (int kt = 0; kt + 1 < KT; ++kt) slab(kt, std::true_type{});
+  slab(KT - 1, std::false_type{});
 
   // epilogue: acc[mi][ni][r] = C[row][col], row = (r/4)*8 + half*4 + r%4, col = lane%32
 #pragma unroll
@@ -164,17 +229,20 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool SCHED>
 void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W, int ldw,
                 void* C, int ldc, const int32_t* dM, int N, int K) {
   const int grid = ((cap_m + BM - 1) / BM) * (N / BN);
   const dim3 blk(WM * WN * 64);
   if (epi == EPI_BF16)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16>), dim3(grid), blk, 0, s, A, lda, W, ldw, C, ldc, dM, N, K);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16, SCHED>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+                       ldc, dM, N, K);
   else if (epi == EPI_RESID)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_RESID>), dim3(grid), blk, 0, s, A, lda, W, ldw, C, ldc, dM, N, K);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_RESID, SCHED>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+                       ldc, dM, N, K);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_SWIGLU>), dim3(grid), blk, 0, s, A, lda, W, ldw, C, ldc, dM, N, K);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_SWIGLU, SCHED>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+                       ldc, dM, N, K);
 }
 
 }  // namespace
@@ -188,11 +256,11 @@ bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, 
   const long tiles256 = (long)((cap_m + 255) / 256) * (N % 256 == 0 ? N / 256 : 0);
   const long tiles128 = (long)((cap_m + 127) / 128) * (N % 128 == 0 ? N / 128 : 0);
   if (N % 256 == 0 && tiles256 >= 256)
-    launch_cfg<256, 256, 2, 2>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+    launch_cfg<256, 256, 4, 2, true>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else if (N % 128 == 0 && tiles128 >= 128)
-    launch_cfg<128, 128, 2, 2>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+    launch_cfg<128, 128, 2, 2, false>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else
-    launch_cfg<64, 64, 1, 1>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+    launch_cfg<64, 64, 1, 1, false>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   return true;
 }
 
