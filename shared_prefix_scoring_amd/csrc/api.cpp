@@ -462,14 +462,25 @@ void plan_add_seq(duolm_ranker* R, Plan& P, int L, int K, int id_off, int id_len
   P.seqs.push_back(sd);
   P.seq_row_off.push_back(P.T);
   const int rp = attn_rows_per_item(false, G), rb = attn_rows_per_item(true, G);
-  for (int r0 = 0; r0 < L; r0 += rp) P.pitems.push_back({s, r0});
-  for (int c0 = 0; c0 < K; c0 += rb) P.bitems.push_back({s, c0});
+  for (int r0 = 0; r0 < L; r0 += rp) P.pitems.push_back({s, r0, P.T, L, K, {0, 0, 0}});
+  for (int c0 = 0; c0 < K; c0 += rb) P.bitems.push_back({s, c0, P.T, L, K, {0, 0, 0}});
   if (head_last) P.head_rows.push_back(P.T + L - 1);
   for (int j = 0; j < K; ++j) P.head_rows.push_back(P.T + L + j);
   P.T += L + K;
 }
 
-void plan_close(Plan& P) { P.seq_row_off.push_back(P.T); }
+// Close a launch: attention tiles go longest first (their key count is the
+// work), so the grid's tail is made of short tiles.
+void plan_close(duolm_ranker* R, Plan& P) {
+  P.seq_row_off.push_back(P.T);
+  const int G = R->dims.n_heads / R->dims.n_kv_heads;
+  const int rp = attn_rows_per_item(false, G);
+  auto pkeys = [&](const WorkItem& w) { return std::min(w.r0 + rp, w.L); };
+  std::stable_sort(P.pitems.begin(), P.pitems.end(),
+                   [&](const WorkItem& a, const WorkItem& b) { return pkeys(a) > pkeys(b); });
+  std::stable_sort(P.bitems.begin(), P.bitems.end(),
+                   [&](const WorkItem& a, const WorkItem& b) { return a.L > b.L; });
+}
 
 // Algorithmic FLOPs and bytes of one launch per kernel class.
 void launch_work(const duolm_ranker* R, const Plan& P, double fl[DUOLM_K_COUNT], double by[DUOLM_K_COUNT]) {
@@ -730,7 +741,7 @@ void build_plans(duolm_ranker* R, const CallInput& in, int mode, std::vector<Pla
     const int L = in.prefix_len[i], K = in.n_cand[i];
     if (mode == DUOLM_MODE_MIS) {
       if (plans.back().T > 0 && plans.back().T + L + K > R->max_rows) {
-        plan_close(plans.back());
+        plan_close(R, plans.back());
         plans.emplace_back();
         plans.back().score_off = score;
       }
@@ -738,7 +749,7 @@ void build_plans(duolm_ranker* R, const CallInput& in, int mode, std::vector<Pla
     } else {
       for (int j = 0; j < K; ++j) {
         if (plans.back().T > 0 && plans.back().T + L + 1 > R->max_rows) {
-          plan_close(plans.back());
+          plan_close(R, plans.back());
           plans.emplace_back();
           plans.back().score_off = score + j;
         }
@@ -748,7 +759,7 @@ void build_plans(duolm_ranker* R, const CallInput& in, int mode, std::vector<Pla
     score += K;
     id_off += L + K;
   }
-  plan_close(plans.back());
+  plan_close(R, plans.back());
 }
 
 int mode_ok(const duolm_opts* o) {

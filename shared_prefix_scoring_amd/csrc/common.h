@@ -29,10 +29,15 @@ struct SeqDesc {
 };
 
 // A tile of query rows: prefix tiles start at row r0 of the sequence,
-// branch tiles at candidate r0.
+// branch tiles at candidate r0.  Carries its sequence's geometry so a
+// workgroup needs one dependent load to start.
 struct WorkItem {
   int32_t seq;
   int32_t r0;
+  int32_t row_off;  // the sequence's first row
+  int32_t L;
+  int32_t K;
+  int32_t pad[3];
 };
 
 struct CallHeader {
@@ -57,16 +62,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// round-to-nearest-even fp32 -> bf16 (NaN kept quiet)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even: one v_cvt_pk_bf16_f32 per pair on gfx950
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {

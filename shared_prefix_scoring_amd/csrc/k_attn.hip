@@ -15,38 +15,72 @@
 // is one (row, query head) pair of the KV head's group) with
 // v_mfma_f32_32x32x16_bf16, so a lane owns one query and 32 of the 64 keys of
 // a tile; then O^T = V^T P^T, so the softmax statistics of a query never
-// leave its lane.  K tiles sit in LDS row-major with a 16-byte-chunk XOR
-// swizzle; V tiles are stored transposed (dims x keys, padded rows).
+// leave its lane.  K and V tiles go global -> LDS directly
+// (global_load_lds_dwordx4, double-buffered: the next tile is in flight while
+// the current one is multiplied).  Both sit row-major (key x dims) with an
+// XOR swizzle of their 16-byte chunks; the V operand of O^T = V^T P^T, which
+// needs 4 consecutive keys of one dim per lane, comes straight out of the
+// row-major tile through the gfx950 LDS transpose read ds_read_b64_tr_b16.
 #include "launch.h"
 
 namespace duolm {
 
 namespace {
 
+#ifndef ATTN_NW
+#define ATTN_NW 8
+#endif
 constexpr int BKV = 64;        // keys per tile
-constexpr int VT_LD = BKV + 4; // padded row of the transposed V tile (elements)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// 16 bytes per lane, global -> LDS; lane i lands at lds + 16 i
+__device__ __forceinline__ void load_lds16(const uint16_t* g, lds_u16_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Within each 16-lane group, lane i gets element i % 4 of the 8-byte reads of
+// lanes 4j + i / 4 (j = 0..3): with lane i addressing row r0 + i / 4 at
+// column c0 + 4 (i % 4) of a row-major 16-bit matrix, it receives column
+// c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ v4i16_t lds_read_tr16(const lds_u16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
+}
 
 // One instantiation serves both row kinds (`branch` is a runtime flag), so a
 // candidate row and a causal row run the very same instruction sequence.
+// V chunk swizzle: the four consecutive keys of a transpose read land in four
+// different 16-chunk quarters of the bank space.
+template <int CPR>
+__device__ __forceinline__ int vswz_t(int key) {
+  return ((key & 3) << 2) & (CPR - 1);
+}
+
 template <int HD, int NW>
 __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ QKV, int ld,
                                                  uint16_t* __restrict__ O, int ldo, DevBatch b, int H,
                                                  int Hkv, float scale_log2, int branch) {
   const bool BRANCH = branch != 0;
-  constexpr int NT = NW * 64;
   constexpr int NKS = HD / 16;  // k-steps of the QK^T product
   constexpr int NDB = HD / 32;  // 32-dim blocks of the output
   constexpr int CPR = HD / 8;   // 16-byte chunks per key row
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * VT_LD];
+  auto vswz = [](int key) { return vswz_t<CPR>(key); };
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][BKV * HD];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][BKV * HD];
 
   const int n_items = BRANCH ? b.hdr->n_bitems : b.hdr->n_pitems;
   if ((int)blockIdx.x >= n_items) return;
   const WorkItem item = (BRANCH ? b.bitems : b.pitems)[blockIdx.x];
-  const SeqDesc sd = b.seqs[item.seq];
+  struct {
+    int row_off, L, K;
+  } const sd = {item.row_off, item.L, item.K};
   const int g = blockIdx.y;  // KV head
   const int G = H / Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qc = wave * 32 + (lane & 31);
   const int lrow = qc / G;
   const int hq = g * G + qc % G;
@@ -75,7 +109,17 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     klim = qrel - 1;
     kend = min(item.r0 + rows_per_item - 1, sd.L - 1);
   }
-  // a wave whose 32 columns are all padding only helps stage tiles
+  // Last key any valid column of this wave needs.  A tile past it is fully
+  // masked for the whole wave: processing it would leave the running max,
+  // sum and output unchanged, so the wave skips its MFMAs.  A wave whose 32
+  // columns are all padding only helps stage tiles.
+  int wave_klim = qvalid ? klim : -1;
+  int wave_kmin = qvalid ? klim : INT32_MAX;  // tiles ending at or before it need no mask
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    wave_klim = max(wave_klim, __shfl_xor(wave_klim, o, 64));
+    wave_kmin = min(wave_kmin, __shfl_xor(wave_kmin, o, 64));
+  }
   const bool wave_active = __any(qvalid);
   const size_t qrow = (size_t)(sd.row_off + qrel);
   const int kcol = H * HD + g * HD;
@@ -95,40 +139,40 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
 
   const uint16_t* seq_base = QKV + (size_t)sd.row_off * ld;
 
-  for (int k0 = 0; k0 < kend; k0 += BKV) {
-    __syncthreads();
-    // K tile, row-major with swizzled chunks
-    for (int c = tid; c < BKV * CPR; c += NT) {
-      const int key = c / CPR, dc = c % CPR;
-      const int kr = min(k0 + key, kend - 1);
-      const uint4 v = *reinterpret_cast<const uint4*>(seq_base + (size_t)kr * ld + kcol + dc * 8);
-      *reinterpret_cast<uint4*>(&Ks[key * HD + ((dc ^ (key % CPR)) << 3)]) = v;
-    }
-    // V tile, transposed: 4 keys x 8 dims per unit, written as 8 x (4 keys)
-    for (int u = tid; u < (BKV / 4) * CPR; u += NT) {
-      const int kq = u / CPR, dc = u % CPR;
-      uint4 v[4];
+  // Tile staging: one global_load_lds_dwordx4 fills 1 KB = 1024 / (2 HD)
+  // consecutive keys.  K chunk dc of key k sits at slot dc ^ (k % CPR), V chunk
+  // dc at slot dc ^ vswz(k); each lane fetches the chunk that belongs at its
+  // slot.  Keys past kend load key kend - 1 (valid memory, masked out).
+  constexpr int KPI = 1024 / (2 * HD);        // keys per load instruction
+  constexpr int NLI = BKV / KPI;              // instructions per tile and matrix
+  constexpr int LPW = (2 * NLI + NW - 1) / NW;  // instructions per wave (K and V)
+  lds_u16_t* ldsK = (lds_u16_t*)(lds_void_t*)&Ks[0][0];
+  lds_u16_t* ldsV = (lds_u16_t*)(lds_void_t*)&Vs[0][0];
+  auto issue = [&](int k0, int buf) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kr = min(k0 + kq * 4 + e, kend - 1);
-        v[e] = *reinterpret_cast<const uint4*>(seq_base + (size_t)kr * ld + vcol + dc * 8);
-      }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int word = dd >> 1, sh = (dd & 1) * 16;
-        auto pick = [&](const uint4& x) -> uint32_t {
-          const uint32_t w = word == 0 ? x.x : word == 1 ? x.y : word == 2 ? x.z : x.w;
-          return (w >> sh) & 0xffffu;
-        };
-        uint2 o;
-        o.x = pick(v[0]) | (pick(v[1]) << 16);
-        o.y = pick(v[2]) | (pick(v[3]) << 16);
-        *reinterpret_cast<uint2*>(&Vt[(dc * 8 + dd) * VT_LD + kq * 4]) = o;
+    for (int j = 0; j < LPW; ++j) {
+      const int ins = wave + j * NW;  // wave-uniform
+      if (ins < 2 * NLI) {
+        const bool isv = ins >= NLI;
+        const int key = (isv ? ins - NLI : ins) * KPI + lane / CPR;
+        const int slot = lane % CPR;
+        const int dc = slot ^ (isv ? vswz(key) : key % CPR);
+        const int kr = min(k0 + key, kend - 1);
+        const uint16_t* src = seq_base + (size_t)kr * ld + (isv ? vcol : kcol) + dc * 8;
+        lds_u16_t* dst = (isv ? ldsV : ldsK) + buf * BKV * HD + (isv ? ins - NLI : ins) * KPI * HD;
+        load_lds16(src, dst);
       }
     }
-    __syncthreads();
-    if (!wave_active) continue;
+  };
 
+  const int ntiles = (kend + BKV - 1) / BKV;
+  if (ntiles > 0) issue(0, 0);
+  wait_loads();
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BKV, buf = t & 1;
+    if (t + 1 < ntiles) issue(k0 + BKV, buf ^ 1);
+    if (wave_active && k0 <= wave_klim) {
     // S^T for two 32-key blocks
     f32x16_t s[2];
 #pragma unroll
@@ -139,23 +183,32 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int dc = ks * 2 + half;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[key * HD + ((dc ^ (key % CPR)) << 3)]);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[buf][key * HD + ((dc ^ (key % CPR)) << 3)]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
     }
-    // mask, scale (log2 domain), tile max
+    // tile max of the raw scores (masked keys -> -inf); the mask is only
+    // evaluated on tiles that reach past some column's last visible key
     float tmax = -INFINITY;
+    if (k0 + BKV - 1 <= wave_kmin) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        const float v = (kk <= klim && kk < kend) ? s[kb][r] * scale_log2 : -INFINITY;
-        s[kb][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          const float v = (kk <= klim && kk < kend) ? s[kb][r] : -INFINITY;
+          s[kb][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(m, tmax);
+    // running max in the log2 domain: scores scaled by log2(e)/sqrt(hd)
+    const float mnew = fmaxf(m, tmax * scale_log2);
     const float msafe = mnew == -INFINITY ? 0.f : mnew;
     const float alpha = exp2f(m - msafe);
     float psum = 0.f;
@@ -163,16 +216,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[kb][r] - msafe);
+        const float p = exp2f(__builtin_fmaf(s[kb][r], scale_log2, -msafe));
         s[kb][r] = p;
         psum += p;
       }
     lsum = __builtin_fmaf(lsum, alpha, psum);
     m = mnew;
+    if (__any(alpha != 1.0f)) {  // multiplying by exactly 1 is a no-op
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
 
     // O^T += V^T P^T over 4 k-steps of 16 keys
 #pragma unroll
@@ -184,14 +239,21 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
       const int key_lo = kb * 32 + (rb >> 2) * 8 + half * 4;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int dim = db * 32 + (lane & 31);
-        const uint2 lo = *reinterpret_cast<const uint2*>(&Vt[dim * VT_LD + key_lo]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&Vt[dim * VT_LD + key_lo + 8]);
-        const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, w);
+        // lanes of a 16-group: dims d0 .. d0 + 15 of keys key_lo .. key_lo + 3
+        // (and + 8 .. + 11); lane i addresses key (i / 4), dims 4 (i % 4) ..
+        const int d0 = db * 32 + ((lane >> 4) & 1) * 16;
+        const int kx = key_lo + ((lane & 15) >> 2);
+        const int dx = d0 + 4 * (lane & 3);
+        const lds_u16_t* vb = ldsV + buf * BKV * HD;
+        const v4i16_t lo = lds_read_tr16(vb + kx * HD + (((dx >> 3) ^ vswz(kx)) << 3) + (dx & 7));
+        const v4i16_t hi = lds_read_tr16(vb + (kx + 8) * HD + (((dx >> 3) ^ vswz(kx + 8)) << 3) + (dx & 7));
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
       }
     }
+    }  // wave computes this tile
+    wait_loads();
+    __syncthreads();
   }
 
   if (wave_active) {
@@ -239,7 +301,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     }
 }
 
-constexpr int NW = 8;  // 256 query columns per workgroup
+constexpr int NW = ATTN_NW;  // query columns per workgroup = 32 NW
 
 template <int HD>
 void launch_hd(hipStream_t s, bool branch, int cap_items, const uint16_t* QKV, int ld, uint16_t* O, int ldo,

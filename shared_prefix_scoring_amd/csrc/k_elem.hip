@@ -104,8 +104,9 @@ void launch_rmsnorm(hipStream_t s, int cap_rows, const float* X, const float* g,
 // Per-head RMSNorm of q and k (gain over head_dim) followed by the rotary
 // embedding at each row's logical position, in place on the bf16 q|k|v row.
 // Rotate-half layout: pair (i, i + hd/2) turns by pos * base^(-2i/hd); the
-// cos/sin table is built on the host in double precision.  One thread per
-// pair; the hd/2 threads of a head reduce with shuffles inside their group.
+// cos/sin table is built on the host in double precision.  Each thread owns
+// 8 consecutive dims (one 16-byte access); a head spans hd/8 threads and the
+// rotation partner of thread t is thread t + hd/16 (fetched by shuffle).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_qk_rope(uint16_t* __restrict__ QKV, int ld,
                                                  const CallHeader* __restrict__ hdr,
@@ -113,35 +114,60 @@ __global__ __launch_bounds__(256) void k_qk_rope(uint16_t* __restrict__ QKV, int
                                                  const float* __restrict__ gq, const float* __restrict__ gk,
                                                  const float2* __restrict__ rope, int H, int Hkv, int hd,
                                                  float eps) {
-  const int half = hd >> 1;
+  const int tph = hd >> 3;  // threads per head: 4, 8 or 16
   const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int i = idx % half;
-  const int rh = idx / half;
+  const int t = idx % tph;
+  const int rh = idx / tph;
   const int nh = H + Hkv;
   const int head = rh % nh;
   const int row = rh / nh;
-  if (row >= hdr->T) return;  // uniform across the head's group (half divides 64)
+  if (row >= hdr->T) return;  // uniform across the head's thread group (tph divides 64)
   const bool isq = head < H;
   const int col = isq ? head * hd : H * hd + (head - H) * hd;
-  const float* g = isq ? gq : gk;
-  uint16_t* p = QKV + (size_t)row * ld + col;
-  const float x1 = bf16_to_f32(p[i]);
-  const float x2 = bf16_to_f32(p[i + half]);
-  float ss = x1 * x1 + x2 * x2;
-  for (int m = half >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, half);
+  const float* g = (isq ? gq : gk) + t * 8;
+  uint16_t* p = QKV + (size_t)row * ld + col + t * 8;
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xffffu));
+    x[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+  for (int m = tph >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, tph);
   const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
-  const float y1 = x1 * inv * g[i];
-  const float y2 = x2 * inv * g[i + half];
-  const float2 cs = rope[(size_t)pos[row] * half + i];
-  p[i] = f32_to_bf16(y1 * cs.x - y2 * cs.y);
-  p[i + half] = f32_to_bf16(y2 * cs.x + y1 * cs.y);
+  float y[8], q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * g[e];
+  const int half_t = tph >> 1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = __shfl_xor(y[e], half_t, tph);  // partner dims (i +- hd/2)
+  const bool lo = t < half_t;
+  const int i0 = (lo ? t : t - half_t) * 8;  // frequency index of dim 0 of this thread
+  const float2* cs = rope + (size_t)pos[row] * (hd >> 1) + i0;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float2 c = cs[e];
+    // first half: x1 cos - x2 sin; second half: x2 cos + x1 sin
+    o[e] = lo ? y[e] * c.x - q[e] * c.y : y[e] * c.x + q[e] * c.y;
+  }
+  uint4 out;
+  out.x = pack_bf16x2(o[0], o[1]);
+  out.y = pack_bf16x2(o[2], o[3]);
+  out.z = pack_bf16x2(o[4], o[5]);
+  out.w = pack_bf16x2(o[6], o[7]);
+  *reinterpret_cast<uint4*>(p) = out;
 }
 
 void launch_qk_rope(hipStream_t s, int cap_rows, uint16_t* QKV, int ld, const CallHeader* hdr,
                     const int32_t* pos, const float* gq, const float* gk, const float2* rope, int H,
                     int Hkv, int hd, float eps) {
   if (cap_rows <= 0) return;
-  const long threads = (long)cap_rows * (H + Hkv) * (hd / 2);
+  const long threads = (long)cap_rows * (H + Hkv) * (hd / 8);
   hipLaunchKernelGGL(k_qk_rope, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, QKV, ld, hdr,
                      pos, gq, gk, rope, H, Hkv, hd, eps);
 }
