@@ -88,12 +88,22 @@ int duolm_load_vid_table(duolm_ranker* r, const uint16_t* rows_fp16, int64_t n_r
 
 int duolm_get_dims(const duolm_ranker* r, duolm_dims* out);
 
-/* One request: prefix ids, then its candidate ids (host pointers). */
+/*
+ * One request: prefix ids, then its candidate ids (host pointers).
+ *
+ * inline_vecs (optional): instead of looking item vectors up in the table,
+ * ship them in the request -- the alternative the pages compare VID ids
+ * against ([digest] 实验结果: ids cut the request size by 99% and raise
+ * throughput).  When non-NULL it holds one fp16 row of d_model values for
+ * every position whose id is >= V, in prefix-then-candidates order, and
+ * those ids only mark the positions (any value >= V); no table is needed.
+ */
 typedef struct {
-  const int32_t* ids;      /* prefix_len ids, each in [0, V + N) */
-  int32_t prefix_len;      /* L >= 1 */
-  const int32_t* cand_ids; /* n_cand ids in [0, V + N) (VIDs in practice) */
-  int32_t n_cand;          /* K >= 1 */
+  const int32_t* ids;          /* prefix_len ids, each in [0, V + N) (or >= V with inline_vecs) */
+  int32_t prefix_len;          /* L >= 1 */
+  const int32_t* cand_ids;     /* n_cand ids in [0, V + N) (VIDs in practice) */
+  int32_t n_cand;              /* K >= 1 */
+  const uint16_t* inline_vecs; /* NULL, or fp16 [number of ids >= V][d_model] */
 } duolm_request;
 
 typedef enum {
@@ -120,7 +130,8 @@ int duolm_score_batch(duolm_ranker* r, const duolm_request* reqs, int32_t n_req,
                       const duolm_opts* opts);
 
 /*
- * Device-resident variant: the ids are already in device memory.
+ * Device-resident variant: the ids are already in device memory (item
+ * vectors always come from the table here).
  *   prefix_len, n_cand : host arrays of n_req lengths.
  *   d_ids              : device, int32, the requests concatenated as
  *                        [prefix_0, cands_0, prefix_1, cands_1, ...].

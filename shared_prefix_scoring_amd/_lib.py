@@ -46,7 +46,8 @@ class duolm_dims(C.Structure):
 
 class duolm_request(C.Structure):
     _fields_ = [("ids", C.POINTER(C.c_int32)), ("prefix_len", C.c_int32),
-                ("cand_ids", C.POINTER(C.c_int32)), ("n_cand", C.c_int32)]
+                ("cand_ids", C.POINTER(C.c_int32)), ("n_cand", C.c_int32),
+                ("inline_vecs", C.c_void_p)]
 
 
 class duolm_opts(C.Structure):
@@ -103,16 +104,24 @@ def _i32(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
 
-def _requests(reqs: Sequence[Tuple[Iterable[int], Iterable[int]]]):
+def _requests(reqs: Sequence[Tuple]):
+    """Requests as (prefix_ids, cand_ids) or (prefix_ids, cand_ids, inline_vecs),
+    inline_vecs an fp16-bits array [number of ids >= V, d_model]."""
     keep = []
     arr = (duolm_request * len(reqs))()
-    for i, (prefix, cands) in enumerate(reqs):
-        p, c = _i32(prefix), _i32(cands)
+    for i, req in enumerate(reqs):
+        p, c = _i32(req[0]), _i32(req[1])
         keep += [p, c]
         arr[i].ids = p.ctypes.data_as(C.POINTER(C.c_int32))
         arr[i].prefix_len = p.shape[0]
         arr[i].cand_ids = c.ctypes.data_as(C.POINTER(C.c_int32))
         arr[i].n_cand = c.shape[0]
+        if len(req) > 2 and req[2] is not None:
+            v = np.ascontiguousarray(req[2], dtype=np.uint16)
+            keep.append(v)
+            arr[i].inline_vecs = v.ctypes.data
+        else:
+            arr[i].inline_vecs = None
     return arr, keep
 
 
@@ -150,7 +159,7 @@ def duolm_get_dims(r) -> duolm_dims:
 
 def duolm_score_batch(r, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None) -> np.ndarray:
     arr, keep = _requests(reqs)
-    n = sum(int(np.asarray(c).shape[0]) for _, c in reqs)
+    n = sum(int(np.asarray(r[1]).shape[0]) for r in reqs)
     out = np.empty(n, dtype=np.float32)
     o = _opts(mode, use_graph, stream)
     _check(lib().duolm_score_batch(r, arr, len(reqs), out.ctypes.data, C.byref(o)))
@@ -231,9 +240,9 @@ class Ranker:
     def stage(self, reqs, layer: int, stage: str, mode: int = DUOLM_MODE_MIS) -> np.ndarray:
         d = self.dims
         if mode == DUOLM_MODE_MIS:
-            T = sum(len(p) + len(c) for p, c in reqs)
+            T = sum(len(r[0]) + len(r[1]) for r in reqs)
         else:
-            T = sum((len(p) + 1) * len(c) for p, c in reqs)
+            T = sum((len(r[0]) + 1) * len(r[1]) for r in reqs)
         width, dt = {
             "attn_norm": (d.d_model, np.uint16), "mlp_norm": (d.d_model, np.uint16),
             "qkv": ((d.n_heads + 2 * d.n_kv_heads) * d.head_dim, np.uint16),

@@ -147,6 +147,9 @@ struct duolm_ranker {
   int32_t* d_ids = nullptr;
   int64_t cap_out = 0;
   float* d_out = nullptr;
+  int64_t cap_inline = 0;
+  uint16_t* d_inline = nullptr;  // this call's inline item vectors (fp16 rows)
+  int32_t call_n_inline = 0;
   int32_t* d_err = nullptr;
   int32_t* h_err = nullptr;  // pinned
   // descriptor block
@@ -421,10 +424,13 @@ int ensure_meta(duolm_ranker* R, int n_seq, int n_pi, int n_bi, int n_hs) {
   return DUOLM_OK;
 }
 
+// Grow a device buffer.  Captured graphs bake buffer addresses, so a
+// reallocation drops them.
 template <typename Tp>
-int ensure_buf(Tp*& ptr, int64_t& cap, int64_t need, hipStream_t s) {
+int ensure_buf(duolm_ranker* R, Tp*& ptr, int64_t& cap, int64_t need) {
   if (need <= cap) return DUOLM_OK;
-  HIP_TRY(hipStreamSynchronize(s));
+  HIP_TRY(hipStreamSynchronize(R->stream));
+  drop_graphs(R);
   if (ptr) (void)hipFree(ptr);
   ptr = nullptr;
   cap = 0;
@@ -584,7 +590,7 @@ void enqueue_forward(Enq& q, const Caps& c) {
   hipStream_t s = q.s;
   DevBatch b = dev_batch(R);
   const int32_t* dT = &b.hdr->T;
-  q.run(DUOLM_K_EMBED, [&] { launch_embed(s, c.T, R->d_ids, b, R->embed, R->vid, D.vocab, R->n_vid, d, R->X, R->pos); });
+  q.run(DUOLM_K_EMBED, [&] { launch_embed(s, c.T, R->d_ids, b, R->embed, R->vid, R->d_inline, D.vocab, R->n_vid, d, R->X, R->pos); });
   if (q.stop(0, DUOLM_STAGE_EMBED)) return;
   for (int l = 0; l < D.n_layers; ++l) {
     const LayerW& W = R->layers[l];
@@ -628,6 +634,7 @@ int upload_plan(duolm_ranker* R, const Plan& P, hipStream_t s) {
   hdr.n_bitems = (int)P.bitems.size();
   hdr.n_scores = (int)P.head_rows.size();
   hdr.score_off = P.score_off;
+  hdr.n_inline = R->call_n_inline;
   memcpy(h, &hdr, sizeof(hdr));
   memcpy(h + R->off_sro, P.seq_row_off.data(), P.seq_row_off.size() * 4);
   memcpy(h + R->off_seq, P.seqs.data(), P.seqs.size() * sizeof(SeqDesc));
@@ -770,7 +777,7 @@ int mode_ok(const duolm_opts* o) {
 // Shared body of the host and device entry points.  `ids` is host memory
 // when ids_dev is false.  Scores go to `out` (host or device).
 int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool ids_dev, float* out, bool out_dev,
-               const duolm_opts* opts) {
+               const duolm_opts* opts, const uint16_t* inline_rows = nullptr, int64_t n_inline = 0) {
   if (!R || !in.prefix_len || !in.n_cand || !ids || !out) return fail(DUOLM_EINVAL, "NULL argument");
   int rc = mode_ok(opts);
   if (rc) return rc;
@@ -782,11 +789,11 @@ int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool id
   if (rc) return rc;
   HIP_TRY(hipSetDevice(R->device));
   if (!ids_dev) {
-    const int64_t lim = (int64_t)R->dims.vocab + R->n_vid;
+    const int64_t lim = (int64_t)R->dims.vocab + R->n_vid + n_inline;
     for (int64_t i = 0; i < total_ids; ++i) {
       const int32_t id = ids[i];
       if (id < 0 || id >= lim) {
-        if (id >= R->dims.vocab && R->n_vid == 0 && id >= 0)
+        if (id >= R->dims.vocab && R->n_vid + n_inline == 0 && id >= 0)
           return fail(DUOLM_ESTATE, "id %d at position %lld is a VID but no item table is loaded", id, (long long)i);
         return fail(DUOLM_ERANGE, "id %d at position %lld outside [0, %lld)", id, (long long)i, (long long)lim);
       }
@@ -804,9 +811,13 @@ int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool id
   }
   if ((rc = ensure_rows(R, maxT))) return rc;
   if ((rc = ensure_meta(R, mseq, mpi, mbi, mhs))) return rc;
-  if ((rc = ensure_buf(R->d_ids, R->cap_ids, total_ids, R->stream))) return rc;
-  if ((rc = ensure_buf(R->d_out, R->cap_out, total_scores, R->stream))) return rc;
+  if ((rc = ensure_buf(R, R->d_ids, R->cap_ids, total_ids))) return rc;
+  if ((rc = ensure_buf(R, R->d_out, R->cap_out, total_scores))) return rc;
+  if ((rc = ensure_buf(R, R->d_inline, R->cap_inline, std::max<int64_t>(1, n_inline) * R->dims.d_model))) return rc;
   if (s != R->stream) HIP_TRY(hipStreamSynchronize(R->stream));
+  R->call_n_inline = (int32_t)n_inline;
+  if (n_inline > 0)
+    HIP_TRY(hipMemcpyAsync(R->d_inline, inline_rows, (size_t)n_inline * R->dims.d_model * 2, hipMemcpyHostToDevice, s));
   HIP_TRY(hipMemcpyAsync(R->d_ids, ids, (size_t)total_ids * 4,
                          ids_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s));
   *R->h_err = 0;
@@ -839,8 +850,11 @@ int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool id
   return DUOLM_OK;
 }
 
-int flatten_requests(const duolm_request* reqs, int n_req, std::vector<int32_t>& L, std::vector<int32_t>& K,
-                     std::vector<int32_t>& ids) {
+// Concatenate host requests as [prefix_0, cands_0, prefix_1, ...].  Requests
+// that ship their item vectors have each id >= V rewritten to V + N + j, row j
+// of the call's inline table.
+int flatten_requests(const duolm_ranker* R, const duolm_request* reqs, int n_req, std::vector<int32_t>& L,
+                     std::vector<int32_t>& K, std::vector<int32_t>& ids, std::vector<uint16_t>& inl) {
   if (!reqs || n_req < 1) return fail(DUOLM_EINVAL, "need n_req >= 1 requests");
   L.resize(n_req);
   K.resize(n_req);
@@ -854,12 +868,38 @@ int flatten_requests(const duolm_request* reqs, int n_req, std::vector<int32_t>&
     total += (size_t)L[i] + K[i];
   }
   ids.resize(total);
+  inl.clear();
+  const int V = R->dims.vocab, d = R->dims.d_model;
+  int64_t n_inl = 0;
   size_t o = 0;
   for (int i = 0; i < n_req; ++i) {
+    const size_t start = o;
     memcpy(&ids[o], reqs[i].ids, (size_t)L[i] * 4);
     o += L[i];
     memcpy(&ids[o], reqs[i].cand_ids, (size_t)K[i] * 4);
     o += K[i];
+    if (!reqs[i].inline_vecs) {
+      const int64_t lim = (int64_t)V + R->n_vid;
+      for (size_t t = start; t < o; ++t) {
+        const int32_t id = ids[t];
+        if (id >= V && R->n_vid == 0)
+          return fail(DUOLM_ESTATE, "request %d: id %d is a VID but no item table is loaded", i, id);
+        if (id < 0 || id >= lim)
+          return fail(DUOLM_ERANGE, "request %d: id %d outside [0, %lld)", i, id, (long long)lim);
+      }
+    } else {
+      int64_t j = 0;
+      for (size_t t = start; t < o; ++t) {
+        if (ids[t] < 0) return fail(DUOLM_ERANGE, "request %d: negative id %d", i, ids[t]);
+        if (ids[t] >= V) {
+          ids[t] = (int32_t)(V + R->n_vid + n_inl + j);
+          ++j;
+        }
+      }
+      if ((int64_t)V + R->n_vid + n_inl + j > INT32_MAX) return fail(DUOLM_EINVAL, "too many inline vectors");
+      inl.insert(inl.end(), reqs[i].inline_vecs, reqs[i].inline_vecs + j * d);
+      n_inl += j;
+    }
   }
   return DUOLM_OK;
 }
@@ -923,10 +963,12 @@ int duolm_score_batch(duolm_ranker* R, const duolm_request* reqs, int32_t n_req,
                       const duolm_opts* opts) {
   if (!R || !scores) return fail(DUOLM_EINVAL, "NULL argument");
   std::vector<int32_t> L, K, ids;
-  int rc = flatten_requests(reqs, n_req, L, K, ids);
+  std::vector<uint16_t> inl;
+  int rc = flatten_requests(R, reqs, n_req, L, K, ids, inl);
   if (rc) return rc;
   CallInput in{L.data(), K.data(), n_req};
-  return score_impl(R, in, ids.data(), false, scores, false, opts);
+  return score_impl(R, in, ids.data(), false, scores, false, opts, inl.data(),
+                    (int64_t)(inl.size() / R->dims.d_model));
 }
 
 int duolm_score_batch_dev(duolm_ranker* R, const int32_t* prefix_len, const int32_t* n_cand, int32_t n_req,
@@ -965,6 +1007,7 @@ void duolm_free_ranker(duolm_ranker* R) {
   if (R->ws) (void)hipFree(R->ws);
   if (R->d_ids) (void)hipFree(R->d_ids);
   if (R->d_out) (void)hipFree(R->d_out);
+  if (R->d_inline) (void)hipFree(R->d_inline);
   if (R->d_err) (void)hipFree(R->d_err);
   if (R->h_err) (void)hipHostFree(R->h_err);
   if (R->d_meta) (void)hipFree(R->d_meta);
@@ -986,8 +1029,10 @@ int duolm_debug_forward(duolm_ranker* R, const duolm_request* reqs, int32_t n_re
   if (layer == R->dims.n_layers && stage != DUOLM_STAGE_LAYER_OUT) return fail(DUOLM_EINVAL, "bad stage");
   if (stage == DUOLM_STAGE_EMBED && layer != 0) return fail(DUOLM_EINVAL, "embed stage is layer 0 only");
   std::vector<int32_t> L, K, ids;
-  int rc = flatten_requests(reqs, n_req, L, K, ids);
+  std::vector<uint16_t> inl;
+  int rc = flatten_requests(R, reqs, n_req, L, K, ids, inl);
   if (rc) return rc;
+  if (!inl.empty()) return fail(DUOLM_EINVAL, "debug forward takes table ids only");
   CallInput in{L.data(), K.data(), n_req};
   int64_t total_ids = 0, total_scores = 0;
   if ((rc = validate_lengths(R, in, total_ids, total_scores))) return rc;
@@ -1013,8 +1058,10 @@ int duolm_debug_forward(duolm_ranker* R, const duolm_request* reqs, int32_t n_re
   if ((rc = ensure_rows(R, P.T))) return rc;
   if ((rc = ensure_meta(R, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size())))
     return rc;
-  if ((rc = ensure_buf(R->d_ids, R->cap_ids, total_ids, R->stream))) return rc;
-  if ((rc = ensure_buf(R->d_out, R->cap_out, total_scores, R->stream))) return rc;
+  if ((rc = ensure_buf(R, R->d_ids, R->cap_ids, total_ids))) return rc;
+  if ((rc = ensure_buf(R, R->d_out, R->cap_out, total_scores))) return rc;
+  if ((rc = ensure_buf(R, R->d_inline, R->cap_inline, (int64_t)R->dims.d_model))) return rc;
+  R->call_n_inline = 0;
   hipStream_t s = R->stream;
   HIP_TRY(hipMemcpyAsync(R->d_ids, ids.data(), ids.size() * 4, hipMemcpyHostToDevice, s));
   *R->h_err = 0;

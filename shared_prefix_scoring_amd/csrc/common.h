@@ -47,7 +47,8 @@ struct CallHeader {
   int32_t n_bitems;  // branch attention tiles
   int32_t n_scores;  // rows read by the score head
   int32_t score_off; // index of this launch's first score in the call's output
-  int32_t pad[10];
+  int32_t n_inline;  // rows of the call's inline item-vector table (ids V+N .. V+N+n_inline-1)
+  int32_t pad[9];
 };
 static_assert(sizeof(CallHeader) == 64, "header layout");
 

@@ -10,13 +10,16 @@ namespace duolm {
 // Embedding gather over the extended vocabulary [0, V + N): ids below V read
 // the bf16 token embedding, ids V + iota read row iota of the fp16 item table
 // ("DuoLM: Fast and Effective Personalized Recommendation with Language
-// Models", 方法步骤详情 step 3).  Both widen exactly to the fp32 residual
-// stream.  Also writes each row's logical position: causal row rho -> rho,
-// every candidate row -> L (same page, 核心方法 / step 4).
+// Models", 方法步骤详情 step 3).  Ids V + N + j read row j of the call's
+// inline item vectors (requests that ship vectors instead of ids).  All widen
+// exactly to the fp32 residual stream.  Also writes each row's logical
+// position: causal row rho -> rho, every candidate row -> L (same page,
+// 核心方法 / step 4).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, DevBatch b,
                                                const uint16_t* __restrict__ E,
-                                               const uint16_t* __restrict__ D, int V, int64_t n_vid,
+                                               const uint16_t* __restrict__ D,
+                                               const uint16_t* __restrict__ Dinl, int V, int64_t n_vid,
                                                int d, float* __restrict__ X, int32_t* __restrict__ pos) {
   const int T = b.hdr->T;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -34,7 +37,7 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, 
   if (lane == 0) pos[row] = rho < sd.L ? rho : sd.L;
   float* xr = X + (size_t)row * d;
   const int nchunk = d >> 3;  // 8 values per chunk
-  if (id < 0 || (int64_t)id >= (int64_t)V + n_vid) {
+  if (id < 0 || (int64_t)id >= (int64_t)V + n_vid + b.hdr->n_inline) {
     if (lane == 0) atomicOr(b.err, 1);
     for (int c = lane; c < nchunk; c += 64) {
       reinterpret_cast<float4*>(xr + c * 8)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -43,7 +46,9 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, 
     return;
   }
   const bool tok = id < V;
-  const uint16_t* src = tok ? E + (size_t)id * d : D + (size_t)(id - V) * d;
+  const int64_t vrow = (int64_t)id - V;
+  const uint16_t* src = tok ? E + (size_t)id * d
+                            : (vrow < n_vid ? D + (size_t)vrow * d : Dinl + (size_t)(vrow - n_vid) * d);
   for (int c = lane; c < nchunk; c += 64) {
     const uint4 v = *reinterpret_cast<const uint4*>(src + c * 8);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -60,9 +65,11 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, 
 }
 
 void launch_embed(hipStream_t s, int cap_rows, const int32_t* ids, DevBatch b, const uint16_t* E,
-                  const uint16_t* D, int V, int64_t n_vid, int d, float* X, int32_t* pos) {
+                  const uint16_t* D, const uint16_t* Dinl, int V, int64_t n_vid, int d, float* X,
+                  int32_t* pos) {
   if (cap_rows <= 0) return;
-  hipLaunchKernelGGL(k_embed, dim3((cap_rows + 3) / 4), dim3(256), 0, s, ids, b, E, D, V, n_vid, d, X, pos);
+  hipLaunchKernelGGL(k_embed, dim3((cap_rows + 3) / 4), dim3(256), 0, s, ids, b, E, D, Dinl, V, n_vid, d, X,
+                     pos);
 }
 
 // ---------------------------------------------------------------------------

@@ -22,7 +22,8 @@ struct DevBatch {
 // the true counts from the CallHeader and idles the surplus, so one captured
 // graph serves any batch up to its caps.
 void launch_embed(hipStream_t s, int cap_rows, const int32_t* ids, DevBatch b, const uint16_t* E,
-                  const uint16_t* D, int V, int64_t n_vid, int d, float* X, int32_t* pos);
+                  const uint16_t* D, const uint16_t* Dinl, int V, int64_t n_vid, int d, float* X,
+                  int32_t* pos);
 void launch_rmsnorm(hipStream_t s, int cap_rows, const float* X, const float* g, uint16_t* Y,
                     const CallHeader* hdr, int d, float eps);
 void launch_qk_rope(hipStream_t s, int cap_rows, uint16_t* QKV, int ld, const CallHeader* hdr,

@@ -204,3 +204,61 @@ def test_profiling_counters(gpu_qwen):
     assert r.kernel_stats("attn_branch").launches == 2 * cfg.n_layers
     assert r.kernel_stats("gemm_qkv").launches == 0
     r.set_profiling([])
+
+
+def _inline_rows(cfg, D, prefix, cands):
+    ids = np.concatenate([prefix, cands])
+    return D[ids[ids >= cfg.vocab] - cfg.vocab]
+
+
+def test_inline_vectors_match_table_lookup(gpu_tiny):
+    # shipping the item vectors in the request gives the same scores, bit for bit
+    cfg, _, D, _, r = gpu_tiny
+    reqs = reqs_of(cfg, 1) + reqs_of(cfg, 4, n=3, n_cand=5)
+    base = r.score(reqs)
+    inl = [(p, c, _inline_rows(cfg, D, p, c)) for p, c in reqs]
+    np.testing.assert_array_equal(r.score(inl), base)
+    np.testing.assert_array_equal(r.score(inl, use_graph=False), base)
+    # mixed batch: one request ships vectors, the others use ids
+    mixed = [inl[0]] + reqs[1:]
+    np.testing.assert_array_equal(r.score(mixed), base)
+
+
+def test_inline_vectors_without_table(tiny):
+    # a ranker with no table loaded scores requests that carry their vectors,
+    # and equals a ranker that holds those vectors in its table
+    cfg, w, D, _ = tiny
+    D2 = synth.make_vid_table(cfg, w, seed=77)
+    with_table = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
+    no_table = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
+    try:
+        with_table.load_vid_table(D2)
+        reqs = reqs_of(cfg, 1)
+        inl = [(p, c, _inline_rows(cfg, D2, p, c)) for p, c in reqs]
+        np.testing.assert_array_equal(no_table.score(inl), with_table.score(reqs))
+    finally:
+        with_table.close()
+        no_table.close()
+
+
+def test_inline_rows_not_addressable_by_ids(gpu_tiny):
+    # the ids just past the table belong to the call's inline rows only: a
+    # request without vectors may not name them
+    cfg, _, D, _, r = gpu_tiny
+    (p, c), = reqs_of(cfg, 1)
+    bad = (np.array([1, 2, cfg.vocab + cfg.n_vid], np.int32), c)
+    with pytest.raises(spa.DuolmError) as e:
+        r.score([(p, c, _inline_rows(cfg, D, p, c)), bad])
+    assert e.value.status == "ERANGE"
+
+
+def test_graph_replay_after_buffer_growth(gpu_qwen):
+    # a bigger call reallocates the id and score buffers: graphs captured
+    # before must not be replayed against the freed buffers
+    cfg, _, _, _, r = gpu_qwen
+    small = reqs_of(cfg, 4, n=2)
+    eager = r.score(small, use_graph=False)
+    np.testing.assert_array_equal(r.score(small, use_graph=True), eager)
+    big = reqs_of(cfg, 3, n=48, seed=5)
+    r.score(big, use_graph=True)
+    np.testing.assert_array_equal(r.score(small, use_graph=True), eager)
