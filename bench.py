@@ -91,6 +91,87 @@ def open_loop(ranker, pool, rate, n_requests, seed, C, use_graph, stream):
     return lat, time.perf_counter() - t0
 
 
+def bench_rating(ranker, cfg, D, C, rounds):
+    """Rating-style regime: 256 requests of K=8 at C=8.  Graph replay against
+    eager launch (device-resident ids), and VID ids against shipping the
+    1024-d fp16 item vectors in the request (host entry point, PCIe-inclusive)."""
+    import torch
+    import synth
+    reqs = synth.make_requests(4, cfg)
+    batches = [reqs[i:i + C] for i in range(0, len(reqs), C)]
+    stream = torch.cuda.current_stream().cuda_stream
+    dev = []
+    for b in batches:
+        ids, L, K = synth.pack_ids(b)
+        dev.append((torch.from_numpy(ids).cuda(), L, K, torch.empty(int(K.sum()), device="cuda")))
+
+    def run_dev(graph):
+        for x in dev:
+            ranker.score_dev(x[1], x[2], x[0].data_ptr(), x[3].data_ptr(), use_graph=graph, stream=stream)
+
+    def as_ids(b):
+        return [(r.prefix, r.cands) for r in b]
+
+    def as_inline(b):
+        out = []
+        for r in b:
+            ids = np.concatenate([r.prefix, r.cands])
+            out.append((r.prefix, r.cands, D[ids[ids >= cfg.vocab] - cfg.vocab]))
+        return out
+
+    host_ids = [as_ids(b) for b in batches]
+    host_inl = [as_inline(b) for b in batches]
+    res = {}
+    for name, fn in [("graph_dev", lambda: run_dev(True)), ("eager_dev", lambda: run_dev(False)),
+                     ("ids_host", lambda: [ranker.score(h, stream=stream) for h in host_ids]),
+                     ("inline_host", lambda: [ranker.score(h, stream=stream) for h in host_inl])]:
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(rounds):
+            fn()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / rounds
+        res[name] = {"requests_per_s": round(len(reqs) / dt, 1), "scores_per_s": round(len(reqs) * 8 / dt, 1),
+                     "ms_per_call": round(dt / len(batches) * 1e3, 3)}
+    ids_bytes = np.mean([4 * (r.L + r.K) for r in reqs])
+    vec_bytes = np.mean([4 * (r.L + r.K) + 2 * cfg.d_model * int(np.sum(np.concatenate([r.prefix, r.cands]) >= cfg.vocab))
+                         for r in reqs])
+    res["payload_bytes_per_request"] = {"ids": round(float(ids_bytes), 1), "inline_vectors": round(float(vec_bytes), 1),
+                                        "cut": round(1 - float(ids_bytes / vec_bytes), 4)}
+    res["launches_per_call"] = "1 graph (graph) or 254 kernels (eager)"
+    return res
+
+
+def bench_stress(ranker, cfg, n_req, n_ind):
+    """L=4096, K=512: MIS over n_req requests in one call, against independent
+    scoring (prefix replicated per candidate, full causal forward) of the
+    first n_ind candidates of the first two requests."""
+    import torch
+    import synth
+    reqs = synth.make_requests(5, cfg, n_requests=n_req)
+    mis_in = [(r.prefix, r.cands) for r in reqs]
+    ranker.score(mis_in)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    mis = ranker.score(mis_in)
+    t_mis = time.perf_counter() - t0
+    ind_in = [(r.prefix, r.cands[:n_ind]) for r in reqs[:2]]
+    ranker.score(ind_in, mode=1)
+    t0 = time.perf_counter()
+    ind = ranker.score(ind_in, mode=1)
+    t_ind = time.perf_counter() - t0
+    ref = np.concatenate([mis[i * 512:i * 512 + n_ind] for i in range(2)])
+    rate_mis = len(mis) / t_mis
+    rate_ind = len(ind) / t_ind
+    return {"mis": {"requests": n_req, "rows": int(sum(r.L + r.K for r in reqs)), "seconds": round(t_mis, 3),
+                    "scores_per_s": round(rate_mis, 1)},
+            "independent": {"sample": f"first {n_ind} candidates of 2 requests", "rows": 2 * n_ind * 4097,
+                            "seconds": round(t_ind, 3), "scores_per_s": round(rate_ind, 1)},
+            "mis_speedup": round(rate_mis / rate_ind, 1),
+            "max_abs_diff_mis_vs_independent": float(np.max(np.abs(ref - ind)))}
+
+
 def traffic_from_profile(kernel_hash):
     p = os.path.join(ROOT, "profiles", "traffic_gemm_gateup.json")
     if not os.path.exists(p):
@@ -115,6 +196,9 @@ def main():
                     help="requests in the Poisson-arrival run (0 disables it)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class (untimed pass)")
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
+    ap.add_argument("--workload", choices=["headline", "rating", "stress"], default="headline",
+                    help="headline: C=64 x K=100 (the metric); rating: K=8 at C=8, graph vs eager and ids vs "
+                         "inline vectors; stress: L=4096 x K=512, MIS vs independent")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -144,6 +228,14 @@ def main():
     D = synth.make_vid_table(cfg, w)
     ranker = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
     ranker.load_vid_table(D)
+    if args.workload != "headline":
+        if args.workload == "rating":
+            res = bench_rating(ranker, cfg, D, C=8, rounds=5)
+        else:
+            res = bench_stress(ranker, cfg, n_req=16, n_ind=32)
+        print(json.dumps({"workload": args.workload, **res}), flush=True)
+        ranker.close()
+        return
     log("generating requests")
     pool = synth.make_requests(3, cfg, n_requests=args.pool)
     C = args.concurrency
