@@ -61,11 +61,13 @@ constexpr int64_t kDefaultMaxRows = 262144;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Bucket an upper bound: smallest m * 2^e >= x with m in [8, 16).
+// Bucket an upper bound: smallest m * 2^e >= x with m in [16, 32], so a
+// graph's grids exceed the true sizes by at most 1/16 (the GEMM tile choice
+// is made on these bounds).
 int bucket(int x) {
-  if (x <= 16) return x <= 0 ? 0 : 16;
+  if (x <= 32) return x <= 0 ? 0 : 32;
   int e = 0;
-  while ((x >> e) >= 16) ++e;
+  while ((x >> e) >= 32) ++e;
   int m = (x + (1 << e) - 1) >> e;
   return m << e;
 }
