@@ -8,8 +8,6 @@
 //     (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks accumulated in fp32;
 //     the large shape is 256 x 256 with 8 waves (two per SIMD, 64 x 128
 //     each), so one wave's LDS and barrier waits overlap the other's MFMAs;
-//     a 192 x 256 shape (8 waves of 96 x 64) cuts the last partial round of
-//     tiles when the row count makes 256-row tiles quantize badly;
 //   * operands go global -> LDS directly with global_load_lds_dwordx4 (one
 //     instruction fills 1 KB of LDS = 8 rows of 128 bytes, lane i writing
 //     bytes [16i, 16i+16)); no staging registers, so the accumulators can
@@ -247,41 +245,22 @@ void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, c
                        ldc, dM, N, K);
 }
 
-int cu_count() {
-  static int n = [] {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    return v;
-  }();
-  return n;
-}
-
 }  // namespace
 
 bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W, int ldw,
                  void* C, int ldc, const int32_t* dM, int N, int K) {
   if (N % 64 != 0 || K % BK != 0 || N <= 0 || K <= 0) return false;
   if (cap_m <= 0) return true;
-  // Tile choice.  Large problems use 256-column tiles, 256 or 192 rows high:
-  // one tile per CU at a time, so the time goes as (rounds of tiles) x (tile
-  // height), and the height with the fewer row-rounds wins (a 192-row tile
-  // turns 336 tiles of a 21.5k x 1024 projection into 448 that still finish
-  // in two rounds, each 3/4 as long).  Every configuration reduces k in the
-  // same order, so the choice never changes a result bit.  Small problems
-  // fall back to 128- or 64-wide tiles.
-  const int ncu = cu_count();
-  const long nt = N % 256 == 0 ? N / 256 : 0;
-  const long tiles256 = (long)((cap_m + 255) / 256) * nt;
+  // Tile choice: the largest tile that still gives at least one block per CU
+  // (256 CUs); small problems fall back to 64-wide tiles.  Every
+  // configuration reduces k in the same order, so the choice never changes a
+  // result bit.  (A 192 x 256 tile that trims the last partial round of the
+  // N = 1024 projections measured slower with these epilogues.)
+  const long tiles256 = (long)((cap_m + 255) / 256) * (N % 256 == 0 ? N / 256 : 0);
   const long tiles128 = (long)((cap_m + 127) / 128) * (N % 128 == 0 ? N / 128 : 0);
-  auto rows_cost = [&](int bm) { return ((((long)cap_m + bm - 1) / bm) * nt + ncu - 1) / ncu * bm; };
-  if (nt && tiles256 >= ncu) {
-    if (rows_cost(192) < rows_cost(256))
-      launch_cfg<192, 256, 2, 4, true>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
-    else
-      launch_cfg<256, 256, 4, 2, true>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
-  } else if (N % 128 == 0 && tiles128 >= 128)
+  if (N % 256 == 0 && tiles256 >= 256)
+    launch_cfg<256, 256, 4, 2, true>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+  else if (N % 128 == 0 && tiles128 >= 128)
     launch_cfg<128, 128, 2, 2, false>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else
     launch_cfg<64, 64, 1, 1, false>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
