@@ -189,7 +189,10 @@ int check_dims(const FileHeader& h) {
     return fail(DUOLM_EINVAL, "bad dimensions in header");
   if (h.n_heads % h.n_kv_heads != 0) return fail(DUOLM_EINVAL, "n_heads %% n_kv_heads != 0");
   const int G = h.n_heads / h.n_kv_heads;
-  if (32 % G != 0) return fail(DUOLM_EINVAL, "query heads per KV head must divide 32");
+  // the attention kernel keeps the rows' own K and V in the query block's
+  // LDS, which holds them only with at least two query heads per KV head
+  if (G < 2 || G > 16 || 16 % G != 0)
+    return fail(DUOLM_EINVAL, "query heads per KV head must be 2, 4, 8 or 16");
   if (!attn_supported(h.head_dim)) return fail(DUOLM_EINVAL, "head_dim must be 32, 64 or 128");
   if (h.d_model % 64 || h.d_ffn % 64 || (h.n_heads * h.head_dim) % 64)
     return fail(DUOLM_EINVAL, "d_model, d_ffn and n_heads*head_dim must be multiples of 64");

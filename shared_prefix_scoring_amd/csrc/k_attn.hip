@@ -59,17 +59,37 @@ __device__ __forceinline__ int vswz_t(int key) {
   return ((key & 3) << 2) & (CPR - 1);
 }
 
+// v_exp_f32: 2^x, results below the normal range flush to zero (a softmax
+// weight that small is dropped either way)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A column keeps exponentiating against a running maximum that may lag its
+// true maximum by up to 2^TAU (so weights stay below 2^TAU, harmless in fp32
+// and bf16), and rescales its sum and output only when a tile's maximum
+// exceeds it by more than that.
+constexpr float kLazyTau = 8.0f;
+
 template <int HD, int NW>
 __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ QKV, int ld,
                                                  uint16_t* __restrict__ O, int ldo, DevBatch b, int H,
                                                  int Hkv, float scale_log2, int branch) {
   const bool BRANCH = branch != 0;
-  constexpr int NKS = HD / 16;  // k-steps of the QK^T product
-  constexpr int NDB = HD / 32;  // 32-dim blocks of the output
-  constexpr int CPR = HD / 8;   // 16-byte chunks per key row
+  constexpr int NKS = HD / 16;         // k-steps of the QK^T product
+  constexpr int NDB = HD / 32;         // 32-dim blocks of the output
+  constexpr int CPR = HD / 8;          // 16-byte chunks per key row / per query column
+  constexpr int NC = NW * 32;          // query columns per workgroup
+  constexpr int TILE = BKV * HD;       // elements of one K or V tile
+  constexpr int QCH = NC * CPR;        // 16-byte chunks of the query block
+  static_assert(QCH % (64 * NW) == 0 && 4 * TILE >= NC * HD, "staging layout");
   auto vswz = [](int key) { return vswz_t<CPR>(key); };
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][BKV * HD];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][BKV * HD];
+  auto cswz = [](int c) { return c & (CPR - 1); };  // chunk swizzle of a query column / own-key row
+  // LDS: K tiles [2] | V tiles [2] | query block.  The query block is copied
+  // to registers first and then holds the rows' own K and V; after the key
+  // loop the tile region stages the output.
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE + NC * HD];
+  uint16_t* const Ks = smem;
+  uint16_t* const Vs = smem + 2 * TILE;
+  uint16_t* const Qs = smem + 4 * TILE;
 
   const int n_items = BRANCH ? b.hdr->n_bitems : b.hdr->n_pitems;
   if ((int)blockIdx.x >= n_items) return;
@@ -84,7 +104,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   const int qc = wave * 32 + (lane & 31);
   const int lrow = qc / G;
   const int hq = g * G + qc % G;
-  const int rows_per_item = NW * 32 / G;
+  const int rows_per_item = NC / G;
+  // the item's query rows, relative to the sequence start, and how many exist
+  const int item_row0 = BRANCH ? sd.L + item.r0 : item.r0;
+  const int item_nrows = min(rows_per_item, (BRANCH ? sd.K : sd.L) - item.r0);
 
   // Every query row sees a run of earlier keys plus its own key.  The earlier
   // keys stream through LDS in 64-key tiles; the row's own (diagonal) key is
@@ -121,23 +144,35 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     wave_kmin = min(wave_kmin, __shfl_xor(wave_kmin, o, 64));
   }
   const bool wave_active = __any(qvalid);
-  const size_t qrow = (size_t)(sd.row_off + qrel);
   const int kcol = H * HD + g * HD;
   const int vcol = H * HD + Hkv * HD + g * HD;
+  const uint16_t* seq_base = QKV + (size_t)sd.row_off * ld;
+  lds_u16_t* const ldsK = (lds_u16_t*)(lds_void_t*)Ks;
+  lds_u16_t* const ldsV = (lds_u16_t*)(lds_void_t*)Vs;
+  lds_u16_t* const ldsQ = (lds_u16_t*)(lds_void_t*)Qs;
+
+  // Query block: column c = (row c / G, head c % G of this KV head's group);
+  // its HD values are one run of 16-byte chunks, chunk k stored at slot
+  // k ^ (c % CPR).  Rows of the G heads are contiguous in memory, so each
+  // load instruction reads whole rows.  Rows past the item's last load the
+  // last row (valid memory, never stored).
+#pragma unroll
+  for (int j = 0; j < QCH / (64 * NW); ++j) {
+    const int c = (wave + j * NW) * 64 + lane;
+    const int col = c / CPR, slot = c % CPR;
+    const int lr = min(col / G, item_nrows - 1);
+    const uint16_t* src =
+        seq_base + (size_t)(item_row0 + lr) * ld + (g * G + col % G) * HD + ((slot ^ cswz(col)) << 3);
+    load_lds16(src, ldsQ + (c - lane) * 8);
+  }
 
   bf16x8_t qf[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8_t*>(QKV + qrow * ld + hq * HD + ks * 16 + half * 8);
-
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m = -INFINITY, lsum = 0.f;
-
-  const uint16_t* seq_base = QKV + (size_t)sd.row_off * ld;
 
   // Tile staging: one global_load_lds_dwordx4 fills 1 KB = 1024 / (2 HD)
   // consecutive keys.  K chunk dc of key k sits at slot dc ^ (k % CPR), V chunk
@@ -146,8 +181,6 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   constexpr int KPI = 1024 / (2 * HD);        // keys per load instruction
   constexpr int NLI = BKV / KPI;              // instructions per tile and matrix
   constexpr int LPW = (2 * NLI + NW - 1) / NW;  // instructions per wave (K and V)
-  lds_u16_t* ldsK = (lds_u16_t*)(lds_void_t*)&Ks[0][0];
-  lds_u16_t* ldsV = (lds_u16_t*)(lds_void_t*)&Vs[0][0];
   auto issue = [&](int k0, int buf) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
@@ -159,7 +192,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
         const int dc = slot ^ (isv ? vswz(key) : key % CPR);
         const int kr = min(k0 + key, kend - 1);
         const uint16_t* src = seq_base + (size_t)kr * ld + (isv ? vcol : kcol) + dc * 8;
-        lds_u16_t* dst = (isv ? ldsV : ldsK) + buf * BKV * HD + (isv ? ins - NLI : ins) * KPI * HD;
+        lds_u16_t* dst = (isv ? ldsV : ldsK) + buf * TILE + (isv ? ins - NLI : ins) * KPI * HD;
         load_lds16(src, dst);
       }
     }
@@ -169,6 +202,26 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   if (ntiles > 0) issue(0, 0);
   wait_loads();
   __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8_t*>(&Qs[qc * HD + (((ks * 2 + half) ^ cswz(qc)) << 3)]);
+  __syncthreads();  // every wave holds its query fragments; the block is free
+
+  // The rows' own K and V into the query block: own-K row r at [r HD], own-V
+  // row r at [(rows_per_item + r) HD], chunk k at slot k ^ (r % CPR).  In
+  // flight while the first key tile is multiplied.
+  {
+    const int sin = QCH / (64 * G);  // load instructions per matrix
+    for (int ins = wave; ins < 2 * sin; ins += NW) {
+      const bool isv = ins >= sin;
+      const int c = (isv ? ins - sin : ins) * 64 + lane;
+      const int r = c / CPR, slot = c % CPR;
+      const int lr = min(r, item_nrows - 1);
+      const uint16_t* src = seq_base + (size_t)(item_row0 + lr) * ld + (isv ? vcol : kcol) + ((slot ^ cswz(r)) << 3);
+      load_lds16(src, ldsQ + (isv ? rows_per_item * HD : 0) + (c - lane) * 8);
+    }
+  }
+
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BKV, buf = t & 1;
     if (t + 1 < ntiles) issue(k0 + BKV, buf ^ 1);
@@ -183,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const int dc = ks * 2 + half;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[buf][key * HD + ((dc ^ (key % CPR)) << 3)]);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[buf * TILE + key * HD + ((dc ^ (key % CPR)) << 3)]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
     }
@@ -208,26 +261,29 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     // running max in the log2 domain: scores scaled by log2(e)/sqrt(hd)
-    const float mnew = fmaxf(m, tmax * scale_log2);
-    const float msafe = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = exp2f(m - msafe);
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(__builtin_fmaf(s[kb][r], scale_log2, -msafe));
-        s[kb][r] = p;
-        psum += p;
-      }
-    lsum = __builtin_fmaf(lsum, alpha, psum);
-    m = mnew;
-    if (__any(alpha != 1.0f)) {  // multiplying by exactly 1 is a no-op
+    const float tl = tmax * scale_log2;
+    const bool grow = tl > m + kLazyTau;  // false for a fully masked tile
+    if (__any(grow)) {                     // other columns multiply by exactly 1
+      const float mnew = grow ? tl : m;
+      const float alpha = grow ? fast_exp2(m - mnew) : 1.0f;
+      lsum *= alpha;
+      m = mnew;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+    const float msafe = m == -INFINITY ? 0.f : m;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -msafe));
+        s[kb][r] = p;
+        psum += p;
+      }
+    lsum += psum;
 
     // O^T += V^T P^T over 4 k-steps of 16 keys
 #pragma unroll
@@ -244,7 +300,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
         const int d0 = db * 32 + ((lane >> 4) & 1) * 16;
         const int kx = key_lo + ((lane & 15) >> 2);
         const int dx = d0 + 4 * (lane & 3);
-        const lds_u16_t* vb = ldsV + buf * BKV * HD;
+        const lds_u16_t* vb = ldsV + buf * TILE;
         const v4i16_t lo = lds_read_tr16(vb + kx * HD + (((dx >> 3) ^ vswz(kx)) << 3) + (dx & 7));
         const v4i16_t hi = lds_read_tr16(vb + (kx + 8) * HD + (((dx >> 3) ^ vswz(kx + 8)) << 3) + (dx & 7));
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -255,50 +311,74 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     wait_loads();
     __syncthreads();
   }
+  wait_loads();     // own K/V (when no key tile was streamed)
+  __syncthreads();
 
   if (wave_active) {
-    // diagonal term: the row's own key and value
-    const uint16_t* kself = QKV + qrow * ld + kcol;
+    // diagonal term: the row's own key and value (own-K row lrow of the block)
+    const uint16_t* kself = Qs + lrow * HD;
     float part = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(kself + ks * 16 + half * 8);
+      const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(kself + (((ks * 2 + half) ^ cswz(lrow)) << 3));
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)qf[ks][e], (float)kv[e], part);
     }
     const float dot = part + __shfl_xor(part, 32, 64);
     const float sv = dot * scale_log2;
-    const float mnew = fmaxf(m, sv);
-    const float alpha = exp2f(m - mnew);
-    const float ps = exp2f(sv - mnew);
-    lsum = __builtin_fmaf(lsum, alpha, half == 0 ? ps : 0.f);
-    m = mnew;
-    const uint16_t* vself = QKV + qrow * ld + vcol;
+    const bool grow = sv > m + kLazyTau;
+    if (__any(grow)) {
+      const float mnew = grow ? sv : m;
+      const float alpha = grow ? fast_exp2(m - mnew) : 1.0f;
+      lsum *= alpha;
+      m = mnew;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float ps = fast_exp2(sv - m);
+    lsum += half == 0 ? ps : 0.f;
+    const uint16_t* vself = Qs + (rows_per_item + lrow) * HD;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const uint2 vv = *reinterpret_cast<const uint2*>(vself + db * 32 + i4 * 8 + half * 4);
+        const uint2 vv = *reinterpret_cast<const uint2*>(vself + (((db * 4 + i4) ^ cswz(lrow)) << 3) + half * 4);
         const float v4[4] = {bf16_to_f32(vv.x & 0xffffu), bf16_to_f32(vv.x >> 16), bf16_to_f32(vv.y & 0xffffu),
                              bf16_to_f32(vv.y >> 16)};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) oacc[db][i4 * 4 + j] = __builtin_fmaf(ps, v4[j], oacc[db][i4 * 4 + j] * alpha);
+        for (int j = 0; j < 4; ++j) oacc[db][i4 * 4 + j] = __builtin_fmaf(ps, v4[j], oacc[db][i4 * 4 + j]);
       }
-  }
-
-  if (!qvalid) return;
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
-  const float inv = 1.0f / ltot;
-  uint16_t* orow = O + qrow * ldo + hq * HD;
+    // normalised output of this column into the tile region, column layout
+    // with the query block's chunk swizzle
+    if (qvalid) {
+      const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+      const float inv = 1.0f / ltot;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      uint2 o;
-      o.x = pack_bf16x2(oacc[db][i4 * 4 + 0] * inv, oacc[db][i4 * 4 + 1] * inv);
-      o.y = pack_bf16x2(oacc[db][i4 * 4 + 2] * inv, oacc[db][i4 * 4 + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + db * 32 + i4 * 8 + half * 4) = o;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          uint2 o;
+          o.x = pack_bf16x2(oacc[db][i4 * 4 + 0] * inv, oacc[db][i4 * 4 + 1] * inv);
+          o.y = pack_bf16x2(oacc[db][i4 * 4 + 2] * inv, oacc[db][i4 * 4 + 3] * inv);
+          *reinterpret_cast<uint2*>(&smem[qc * HD + (((db * 4 + i4) ^ cswz(qc)) << 3) + half * 4]) = o;
+        }
     }
+  }
+  __syncthreads();
+  // rows of the item: G heads x HD contiguous per row, 16 bytes per lane
+  uint16_t* const obase = O + (size_t)(sd.row_off + item_row0) * ldo + g * G * HD;
+#pragma unroll
+  for (int j = 0; j < QCH / (64 * NW); ++j) {
+    const int c = (wave + j * NW) * 64 + lane;
+    const int col = c / CPR, slot = c % CPR;
+    const int lr = col / G;
+    if (lr < item_nrows) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&smem[c * 8]);
+      *reinterpret_cast<uint4*>(obase + (size_t)lr * ldo + (col % G) * HD + ((slot ^ cswz(col)) << 3)) = v;
+    }
+  }
 }
 
 constexpr int NW = ATTN_NW;  // query columns per workgroup = 32 NW

@@ -57,7 +57,7 @@ def test_bad_magic_and_short_blob(tmp_path):
 
 def test_unsupported_dims_rejected():
     import dataclasses
-    for bad in (dict(head_dim=48), dict(n_kv_heads=3), dict(d_ffn=100)):
+    for bad in (dict(head_dim=48), dict(n_kv_heads=3), dict(n_kv_heads=4), dict(d_ffn=100)):
         cfg = dataclasses.replace(synth.TINY, **bad)
         try:
             w = synth.make_weights(cfg)
