@@ -75,36 +75,61 @@ void launch_embed(hipStream_t s, int cap_rows, const int32_t* ids, DevBatch b, c
 // ---------------------------------------------------------------------------
 // RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, fp32 math, bf16 out.
 // ---------------------------------------------------------------------------
+// One wave per row.  The row stays in registers between the sum of squares
+// and the scaling (NQ float4 per lane; NQ = 0 loops over the row instead).
+template <int NQ>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ X, const float* __restrict__ g,
                                                  uint16_t* __restrict__ Y, const CallHeader* __restrict__ hdr,
                                                  int d, float eps) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= hdr->T) return;
-  const float* xr = X + (size_t)row * d;
-  const int nq = d >> 2;
+  const float4* xr = reinterpret_cast<const float4*>(X + (size_t)row * d);
+  const float4* gr = reinterpret_cast<const float4*>(g);
+  uint2* yr = reinterpret_cast<uint2*>(Y + (size_t)row * d);
   float ss = 0.f;
-  for (int c = lane; c < nq; c += 64) {
-    const float4 v = reinterpret_cast<const float4*>(xr)[c];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  uint16_t* yr = Y + (size_t)row * d;
-  for (int c = lane; c < nq; c += 64) {
-    const float4 v = reinterpret_cast<const float4*>(xr)[c];
-    const float4 gg = reinterpret_cast<const float4*>(g)[c];
-    uint2 o;
-    o.x = pack_bf16x2(v.x * inv * gg.x, v.y * inv * gg.y);
-    o.y = pack_bf16x2(v.z * inv * gg.z, v.w * inv * gg.w);
-    reinterpret_cast<uint2*>(yr)[c] = o;
+  if constexpr (NQ > 0) {
+    float4 v[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) v[j] = xr[lane + 64 * j];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const float4 gg = gr[lane + 64 * j];
+      uint2 o;
+      o.x = pack_bf16x2(v[j].x * inv * gg.x, v[j].y * inv * gg.y);
+      o.y = pack_bf16x2(v[j].z * inv * gg.z, v[j].w * inv * gg.w);
+      yr[lane + 64 * j] = o;
+    }
+  } else {
+    const int nq = d >> 2;
+    for (int c = lane; c < nq; c += 64) {
+      const float4 v = xr[c];
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int c = lane; c < nq; c += 64) {
+      const float4 v = xr[c];
+      const float4 gg = gr[c];
+      uint2 o;
+      o.x = pack_bf16x2(v.x * inv * gg.x, v.y * inv * gg.y);
+      o.y = pack_bf16x2(v.z * inv * gg.z, v.w * inv * gg.w);
+      yr[c] = o;
+    }
   }
 }
 
 void launch_rmsnorm(hipStream_t s, int cap_rows, const float* X, const float* g, uint16_t* Y,
                     const CallHeader* hdr, int d, float eps) {
   if (cap_rows <= 0) return;
-  hipLaunchKernelGGL(k_rmsnorm, dim3((cap_rows + 3) / 4), dim3(256), 0, s, X, g, Y, hdr, d, eps);
+  const dim3 grid((cap_rows + 3) / 4), blk(256);
+  if (d == 1024) hipLaunchKernelGGL(k_rmsnorm<4>, grid, blk, 0, s, X, g, Y, hdr, d, eps);
+  else if (d == 2048) hipLaunchKernelGGL(k_rmsnorm<8>, grid, blk, 0, s, X, g, Y, hdr, d, eps);
+  else hipLaunchKernelGGL(k_rmsnorm<0>, grid, blk, 0, s, X, g, Y, hdr, d, eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -113,7 +138,9 @@ void launch_rmsnorm(hipStream_t s, int cap_rows, const float* X, const float* g,
 // Rotate-half layout: pair (i, i + hd/2) turns by pos * base^(-2i/hd); the
 // cos/sin table is built on the host in double precision.  Each thread owns
 // 8 consecutive dims (one 16-byte access); a head spans hd/8 threads and the
-// rotation partner of thread t is thread t + hd/16 (fetched by shuffle).
+// rotation partner of thread t is thread t + hd/16 (fetched by shuffle).  A
+// wave walks the heads of one row, so the row's table entries and the gains
+// are read once per row rather than once per head.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_qk_rope(uint16_t* __restrict__ QKV, int ld,
                                                  const CallHeader* __restrict__ hdr,
@@ -121,62 +148,70 @@ __global__ __launch_bounds__(256) void k_qk_rope(uint16_t* __restrict__ QKV, int
                                                  const float* __restrict__ gq, const float* __restrict__ gk,
                                                  const float2* __restrict__ rope, int H, int Hkv, int hd,
                                                  float eps) {
+  // one wave per row; lane = (head slot, thread t of the head); the cos/sin
+  // of the row's position and the gains are loaded once and serve every head
   const int tph = hd >> 3;  // threads per head: 4, 8 or 16
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int t = idx % tph;
-  const int rh = idx / tph;
-  const int nh = H + Hkv;
-  const int head = rh % nh;
-  const int row = rh / nh;
-  if (row >= hdr->T) return;  // uniform across the head's thread group (tph divides 64)
-  const bool isq = head < H;
-  const int col = isq ? head * hd : H * hd + (head - H) * hd;
-  const float* g = (isq ? gq : gk) + t * 8;
-  uint16_t* p = QKV + (size_t)row * ld + col + t * 8;
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float x[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xffffu));
-    x[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-  for (int m = tph >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, tph);
-  const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
-  float y[8], q[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * g[e];
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= hdr->T) return;
+  const int lane = threadIdx.x & 63;
+  const int t = lane % tph;
+  const int slot = lane / tph;
+  const int slots = 64 / tph;
   const int half_t = tph >> 1;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) q[e] = __shfl_xor(y[e], half_t, tph);  // partner dims (i +- hd/2)
   const bool lo = t < half_t;
   const int i0 = (lo ? t : t - half_t) * 8;  // frequency index of dim 0 of this thread
   const float2* cs = rope + (size_t)pos[row] * (hd >> 1) + i0;
-  float o[8];
+  float2 c[8];
+  float g_q[8], g_k[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float2 c = cs[e];
-    // first half: x1 cos - x2 sin; second half: x2 cos + x1 sin
-    o[e] = lo ? y[e] * c.x - q[e] * c.y : y[e] * c.x + q[e] * c.y;
+    c[e] = cs[e];
+    g_q[e] = gq[t * 8 + e];
+    g_k[e] = gk[t * 8 + e];
   }
-  uint4 out;
-  out.x = pack_bf16x2(o[0], o[1]);
-  out.y = pack_bf16x2(o[2], o[3]);
-  out.z = pack_bf16x2(o[4], o[5]);
-  out.w = pack_bf16x2(o[6], o[7]);
-  *reinterpret_cast<uint4*>(p) = out;
+  uint16_t* rowp = QKV + (size_t)row * ld;
+  for (int head = slot; head < H + Hkv; head += slots) {
+    const bool isq = head < H;
+    uint16_t* p = rowp + (isq ? head * hd : H * hd + (head - H) * hd) + t * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xffffu));
+      x[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+    for (int m = tph >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, tph);
+    const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
+    float y[8], q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * (isq ? g_q[e] : g_k[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = __shfl_xor(y[e], half_t, tph);  // partner dims (i +- hd/2)
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // first half: x1 cos - x2 sin; second half: x2 cos + x1 sin
+      o[e] = lo ? y[e] * c[e].x - q[e] * c[e].y : y[e] * c[e].x + q[e] * c[e].y;
+    }
+    uint4 out;
+    out.x = pack_bf16x2(o[0], o[1]);
+    out.y = pack_bf16x2(o[2], o[3]);
+    out.z = pack_bf16x2(o[4], o[5]);
+    out.w = pack_bf16x2(o[6], o[7]);
+    *reinterpret_cast<uint4*>(p) = out;
+  }
 }
 
 void launch_qk_rope(hipStream_t s, int cap_rows, uint16_t* QKV, int ld, const CallHeader* hdr,
                     const int32_t* pos, const float* gq, const float* gk, const float2* rope, int H,
                     int Hkv, int hd, float eps) {
   if (cap_rows <= 0) return;
-  const long threads = (long)cap_rows * (H + Hkv) * (hd / 8);
-  hipLaunchKernelGGL(k_qk_rope, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, QKV, ld, hdr,
-                     pos, gq, gk, rope, H, Hkv, hd, eps);
+  hipLaunchKernelGGL(k_qk_rope, dim3((unsigned)((cap_rows + 3) / 4)), dim3(256), 0, s, QKV, ld, hdr, pos, gq, gk,
+                     rope, H, Hkv, hd, eps);
 }
 
 // ---------------------------------------------------------------------------
