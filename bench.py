@@ -172,6 +172,79 @@ def bench_stress(ranker, cfg, n_req, n_ind):
             "max_abs_diff_mis_vs_independent": float(np.max(np.abs(ref - ind)))}
 
 
+def summarize_traffic(out_dir, warmup, steps, pool_size):
+    """Turn the four counter passes (FETCH_SIZE and WRITE_SIZE of the gate/up
+    GEMM in an eager `--no-graph --open-loop 0 --cpu-baseline-s 0` run with the
+    given warmup/steps, and of the copy kernel under --calib-copy) into
+    profiles/traffic_gemm_gateup.json.  Each counter is scaled by what it
+    reads for the copy kernel's known bytes."""
+    import csv
+
+    import synth
+
+    def per_dispatch(d, counter, name_part):
+        vals = []
+        for root, _, files in os.walk(os.path.join(out_dir, d)):
+            for fn in files:
+                if not fn.endswith("counter_collection.csv"):
+                    continue
+                with open(os.path.join(root, fn)) as f:
+                    for r in csv.DictReader(f):
+                        if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                            vals.append(float(r["Counter_Value"]))
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {name_part} under {d}")
+        return sum(vals) / len(vals), len(vals)
+
+    gate = "k_gemm<256, 256, 4, 2, 2,"
+    f_kib, n = per_dispatch("tr_f", "FETCH_SIZE", gate)
+    w_kib, _ = per_dispatch("tr_w", "WRITE_SIZE", gate)
+    cf_kib, _ = per_dispatch("cal_f", "FETCH_SIZE", "k_copy")
+    cw_kib, _ = per_dispatch("cal_w", "WRITE_SIZE", "k_copy")
+    copy_kib = (1 << 30) / 1024.0
+    fs, ws = copy_kib / cf_kib, copy_kib / cw_kib
+    cfg = synth.QWEN3_0P6B
+    pool = synth.make_requests(3, cfg, n_requests=pool_size)
+    calls = warmup + steps
+    rows = [sum(r.L + r.K for r in pool[i * 64:(i + 1) * 64]) for i in range(calls)]
+    t_mean = sum(rows) / len(rows)
+    d, f = cfg.d_model, cfg.d_ffn
+    alg = 2 * f * d * 2 + t_mean * (d * 2 + f * 2)  # weights + activations in + SwiGLU out (bf16)
+    meas = (f_kib * fs + w_kib * ws) * 1024.0
+    out = {
+        "kernel": "k_gemm<256, 256, 4, 2, EPI_SWIGLU> (gate/up projection + SwiGLU epilogue)",
+        "workload": f"bench.py workload: 0.6B-shaped ranker, 64 requests x 100 candidates per call, eager launches, "
+                    f"{calls} calls x {cfg.n_layers} layers",
+        "commands": [
+            "cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'k_gemm|k_copy' -d $REPO/gpurun_out/traffic/tr_f "
+            f"-o f -f csv -- python -u $REPO/bench.py --steps {steps} --warmup {warmup} --no-graph --cpu-baseline-s 0 --open-loop 0",
+            "cd /tmp && rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'k_gemm|k_copy' -d $REPO/gpurun_out/traffic/tr_w "
+            f"-o w -f csv -- python -u $REPO/bench.py --steps {steps} --warmup {warmup} --no-graph --cpu-baseline-s 0 --open-loop 0",
+            "cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-include-regex k_copy -d $REPO/gpurun_out/traffic/cal_f -o f -f csv "
+            "-- python -u $REPO/bench.py --calib-copy",
+            "cd /tmp && rocprofv3 --pmc WRITE_SIZE --kernel-include-regex k_copy -d $REPO/gpurun_out/traffic/cal_w -o w -f csv "
+            "-- python -u $REPO/bench.py --calib-copy",
+            f"python bench.py --summarize-traffic gpurun_out/traffic --steps {steps} --warmup {warmup}",
+        ],
+        "calibration": {"copy_kernel": "k_copy, 1 GiB read + 1 GiB written",
+                        "FETCH_SIZE_KiB_per_launch": round(cf_kib, 1), "WRITE_SIZE_KiB_per_launch": round(cw_kib, 1),
+                        "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+        "launches": n,
+        "mean_rows_per_launch": round(t_mean),
+        "FETCH_SIZE_KiB_per_launch": round(f_kib, 1),
+        "WRITE_SIZE_KiB_per_launch": round(w_kib, 1),
+        "bytes_per_launch": round(meas),
+        "algorithmic_bytes_per_launch": round(alg),
+        "ratio_measured_to_algorithmic": round(meas / alg, 2),
+        "kernel_src_hash": src_hash("k_gemm.hip", "common.h", "launch.h"),
+    }
+    path = os.path.join(ROOT, "profiles", "traffic_gemm_gateup.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out), flush=True)
+
+
 def traffic_from_profile(kernel_hash):
     p = os.path.join(ROOT, "profiles", "traffic_gemm_gateup.json")
     if not os.path.exists(p):
@@ -196,10 +269,16 @@ def main():
                     help="requests in the Poisson-arrival run (0 disables it)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class (untimed pass)")
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
+    ap.add_argument("--summarize-traffic", metavar="DIR",
+                    help="write profiles/traffic_gemm_gateup.json from the counter runs under DIR (no GPU)")
     ap.add_argument("--workload", choices=["headline", "rating", "stress"], default="headline",
                     help="headline: C=64 x K=100 (the metric); rating: K=8 at C=8, graph vs eager and ids vs "
                          "inline vectors; stress: L=4096 x K=512, MIS vs independent")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, args.warmup, args.steps, args.pool)
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU scaling is not implemented "
