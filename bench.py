@@ -143,6 +143,37 @@ def bench_rating(ranker, cfg, D, C, rounds):
     return res
 
 
+def bench_latency(ranker, cfg, calls):
+    """One request at a time (L = 452, K = 100): per-call latency with graph
+    replay and eagerly, device-resident ids and the host entry point."""
+    import torch
+    import synth
+    (req,) = synth.make_requests(2, cfg)
+    ids, L, K = synth.pack_ids([req])
+    d_ids = torch.from_numpy(ids).cuda()
+    d_s = torch.empty(int(K.sum()), device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {"request": {"L": int(req.L), "K": int(req.K)}}
+    for name, fn in [
+        ("graph_dev", lambda: ranker.score_dev(L, K, d_ids.data_ptr(), d_s.data_ptr(), use_graph=True, stream=stream)),
+        ("eager_dev", lambda: ranker.score_dev(L, K, d_ids.data_ptr(), d_s.data_ptr(), use_graph=False, stream=stream)),
+        ("graph_host", lambda: ranker.score([(req.prefix, req.cands)], use_graph=True, stream=stream)),
+    ]:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(calls):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            t.append((time.perf_counter() - t0) * 1e3)
+        t = np.array(t)
+        res[name] = {"p50_ms": round(float(np.median(t)), 3), "p99_ms": round(float(np.percentile(t, 99)), 3),
+                     "scores_per_s": round(float(req.K / np.median(t) * 1e3), 1)}
+    return res
+
+
 def bench_stress(ranker, cfg, n_req, n_ind):
     """L=4096, K=512: MIS over n_req requests in one call, against independent
     scoring (prefix replicated per candidate, full causal forward) of the
@@ -271,9 +302,10 @@ def main():
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
     ap.add_argument("--summarize-traffic", metavar="DIR",
                     help="write profiles/traffic_gemm_gateup.json from the counter runs under DIR (no GPU)")
-    ap.add_argument("--workload", choices=["headline", "rating", "stress"], default="headline",
-                    help="headline: C=64 x K=100 (the metric); rating: K=8 at C=8, graph vs eager and ids vs "
-                         "inline vectors; stress: L=4096 x K=512, MIS vs independent")
+    ap.add_argument("--workload", choices=["headline", "latency", "rating", "stress"], default="headline",
+                    help="headline: C=64 x K=100 (the metric); latency: one L=452 x K=100 request per call; "
+                         "rating: K=8 at C=8, graph vs eager and ids vs inline vectors; stress: L=4096 x K=512, "
+                         "MIS vs independent")
     args = ap.parse_args()
 
     if args.summarize_traffic:
@@ -310,6 +342,8 @@ def main():
     if args.workload != "headline":
         if args.workload == "rating":
             res = bench_rating(ranker, cfg, D, C=8, rounds=5)
+        elif args.workload == "latency":
+            res = bench_latency(ranker, cfg, calls=100)
         else:
             res = bench_stress(ranker, cfg, n_req=16, n_ind=32)
         print(json.dumps({"workload": args.workload, **res}), flush=True)
