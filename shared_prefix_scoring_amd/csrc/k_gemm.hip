@@ -221,7 +221,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
 #pragma unroll
         for (int ni = 0; ni < NI; ni += 2) {
           const float g = acc[mi][ni][r], u = acc[mi][ni + 1][r];
-          const float h = g / (1.0f + __expf(-g)) * u;
+          // silu(g) u with the hardware reciprocal (about 1 ulp; the result
+          // is rounded to bf16)
+          const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
           C[(n0 + wn * WTN + ni * 32) / 2 + (lane & 31)] = f32_to_bf16(h);
         }
       }
