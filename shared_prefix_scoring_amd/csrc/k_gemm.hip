@@ -202,6 +202,32 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   slab(KT - 1, std::false_type{});
 
   // epilogue: acc[mi][ni][r] = C[row][col], row = (r/4)*8 + half*4 + r%4, col = lane%32
+  if constexpr (EPI == EPI_RESID) {
+    // residual add, one 32-row strip at a time: every load of the strip is in
+    // flight before the first add (rows past M read row M - 1 and are not
+    // stored), so the strip pays one memory latency instead of one per row
+    float* C = reinterpret_cast<float*>(Cv);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      float xv[16][NI];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = min(m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3), M - 1);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) xv[r][ni] = C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+        if (row < M) {
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)] = xv[r][ni] + acc[mi][ni][r];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -212,10 +238,6 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
         uint16_t* C = reinterpret_cast<uint16_t*>(Cv) + (size_t)row * ldc;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) C[n0 + wn * WTN + ni * 32 + (lane & 31)] = f32_to_bf16(acc[mi][ni][r]);
-      } else if constexpr (EPI == EPI_RESID) {
-        float* C = reinterpret_cast<float*>(Cv) + (size_t)row * ldc;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) C[n0 + wn * WTN + ni * 32 + (lane & 31)] += acc[mi][ni][r];
       } else {
         uint16_t* C = reinterpret_cast<uint16_t*>(Cv) + (size_t)row * ldc;
 #pragma unroll
