@@ -269,20 +269,40 @@ void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, c
                        ldc, dM, N, K);
 }
 
+int cu_count() {
+  static const int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    return v;
+  }();
+  return n;
+}
+
 }  // namespace
 
 bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W, int ldw,
                  void* C, int ldc, const int32_t* dM, int N, int K) {
   if (N % 64 != 0 || K % BK != 0 || N <= 0 || K <= 0) return false;
   if (cap_m <= 0) return true;
-  // Tile choice: the largest tile that still gives at least one block per CU
-  // (256 CUs); small problems fall back to 64-wide tiles.  Every
-  // configuration reduces k in the same order, so the choice never changes a
-  // result bit.  (A 192 x 256 tile that trims the last partial round of the
-  // N = 1024 projections measured slower with these epilogues.)
-  const long tiles256 = (long)((cap_m + 255) / 256) * (N % 256 == 0 ? N / 256 : 0);
+  // Tile choice: the largest tile that still gives at least one block per CU;
+  // small problems fall back to 64-wide tiles.  Every configuration reduces k
+  // in the same order, so the choice never changes a result bit.  With one
+  // tile per CU at a time, a launch takes (rounds of tiles) x (tile time); for
+  // the residual projections (N = 1024: 336 tiles of 256 rows at T = 21.5k, a
+  // two-round launch whose second round is a third full) 192-row tiles finish
+  // in the same number of rounds with 3/4 of the work each, and are used
+  // when they need fewer row-rounds.  (With the bf16 and SwiGLU epilogues the
+  // 192-row tile measured slower.)
+  const int ncu = cu_count();
+  const long nt = N % 256 == 0 ? N / 256 : 0;
+  const long tiles256 = (long)((cap_m + 255) / 256) * nt;
   const long tiles128 = (long)((cap_m + 127) / 128) * (N % 128 == 0 ? N / 128 : 0);
-  if (N % 256 == 0 && tiles256 >= 256)
+  auto row_rounds = [&](int bm) { return ((((long)cap_m + bm - 1) / bm) * nt + ncu - 1) / ncu * bm; };
+  if (nt && tiles256 >= ncu && epi == EPI_RESID && row_rounds(192) < row_rounds(256))
+    launch_cfg<192, 256, 2, 4, true>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+  else if (nt && tiles256 >= ncu)
     launch_cfg<256, 256, 4, 2, true>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else if (N % 128 == 0 && tiles128 >= 128)
     launch_cfg<128, 128, 2, 2, false>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);

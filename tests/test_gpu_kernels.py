@@ -31,7 +31,7 @@ GEMM_SHAPES = [
     (1, 64, 64), (77, 256, 128), (300, 768, 384), (513, 4096, 1024),   # 64x64 tiles, ragged M
     (4100, 1024, 2048), (1500, 3072, 1024),                          # 128x128 tiles
     (4096, 4096, 1024), (4133, 6144, 1024),                          # 256x256 tiles, ragged tail
-    (16500, 1024, 256), (12000, 2048, 64),                           # many 256x256 tiles, short K, ragged
+    (16500, 1024, 256), (12000, 2048, 64),                           # 256-row tiles, or 192-row for the residual epilogue
 ]
 
 
