@@ -80,16 +80,20 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   constexpr int NC = NW * 32;          // query columns per workgroup
   constexpr int TILE = BKV * HD;       // elements of one K or V tile
   constexpr int QCH = NC * CPR;        // 16-byte chunks of the query block
-  static_assert(QCH % (64 * NW) == 0 && 4 * TILE >= NC * HD, "staging layout");
+  static_assert(QCH % (64 * NW) == 0, "staging layout");
   auto vswz = [](int key) { return vswz_t<CPR>(key); };
   auto cswz = [](int c) { return c & (CPR - 1); };  // chunk swizzle of a query column / own-key row
-  // LDS: K tiles [2] | V tiles [2] | query block.  The query block is copied
-  // to registers first and then holds the rows' own K and V; after the key
-  // loop the tile region stages the output.
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE + NC * HD];
-  uint16_t* const Ks = smem;
-  uint16_t* const Vs = smem + 2 * TILE;
-  uint16_t* const Qs = smem + 4 * TILE;
+  // LDS: K and V tiles per pipeline stage, and the query block.  The query
+  // block is copied to registers first, then holds the rows' own K and V,
+  // and finally stages the output.  Each stage is an array of its own, so the
+  // compiler can see that reads of one stage never touch the global->LDS
+  // copies in flight into the other (one array indexed by a runtime stage
+  // made it wait for those copies before every V read).
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Qs[NC * HD];
 
   const int n_items = BRANCH ? b.hdr->n_bitems : b.hdr->n_pitems;
   if ((int)blockIdx.x >= n_items) return;
@@ -147,9 +151,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   const int kcol = H * HD + g * HD;
   const int vcol = H * HD + Hkv * HD + g * HD;
   const uint16_t* seq_base = QKV + (size_t)sd.row_off * ld;
-  lds_u16_t* const ldsK = (lds_u16_t*)(lds_void_t*)Ks;
-  lds_u16_t* const ldsV = (lds_u16_t*)(lds_void_t*)Vs;
   lds_u16_t* const ldsQ = (lds_u16_t*)(lds_void_t*)Qs;
+  // stage ST's K and V tiles
+  auto kt = [&](auto st) -> uint16_t* { if constexpr (decltype(st)::value == 0) return sK0; else return sK1; };
+  auto vt = [&](auto st) -> uint16_t* { if constexpr (decltype(st)::value == 0) return sV0; else return sV1; };
 
   // Query block: column c = (row c / G, head c % G of this KV head's group);
   // its HD values are one run of 16-byte chunks, chunk k stored at slot
@@ -181,7 +186,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   constexpr int KPI = 1024 / (2 * HD);        // keys per load instruction
   constexpr int NLI = BKV / KPI;              // instructions per tile and matrix
   constexpr int LPW = (2 * NLI + NW - 1) / NW;  // instructions per wave (K and V)
-  auto issue = [&](int k0, int buf) {
+  auto issue = [&](int k0, auto st) {
+    lds_u16_t* const dK = (lds_u16_t*)(lds_void_t*)kt(st);
+    lds_u16_t* const dV = (lds_u16_t*)(lds_void_t*)vt(st);
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int ins = wave + j * NW;  // wave-uniform
@@ -192,14 +199,16 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
         const int dc = slot ^ (isv ? vswz(key) : key % CPR);
         const int kr = min(k0 + key, kend - 1);
         const uint16_t* src = seq_base + (size_t)kr * ld + (isv ? vcol : kcol) + dc * 8;
-        lds_u16_t* dst = (isv ? ldsV : ldsK) + buf * TILE + (isv ? ins - NLI : ins) * KPI * HD;
+        lds_u16_t* dst = (isv ? dV : dK) + (isv ? ins - NLI : ins) * KPI * HD;
         load_lds16(src, dst);
       }
     }
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
   const int ntiles = (kend + BKV - 1) / BKV;
-  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 0) issue(0, S0{});
   wait_loads();
   __syncthreads();
 #pragma unroll
@@ -222,23 +231,37 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     }
   }
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * BKV, buf = t & 1;
-    if (t + 1 < ntiles) issue(k0 + BKV, buf ^ 1);
+  auto tile = [&](int t, auto st) {
+    constexpr int ST = decltype(st)::value;
+    const int k0 = t * BKV;
+    if (t + 1 < ntiles) issue(k0 + BKV, std::integral_constant<int, ST ^ 1>{});
+    const uint16_t* const Kt = kt(st);
+    const lds_u16_t* const vb = (const lds_u16_t*)(lds_void_t*)vt(st);
     if (wave_active && k0 <= wave_klim) {
-    // S^T for two 32-key blocks
+    // S^T for two 32-key blocks, the two accumulation chains interleaved and
+    // each k-step's key fragments read one step ahead
     f32x16_t s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int key = kb * 32 + (lane & 31);
+    const int key0 = lane & 31, key1 = 32 + (lane & 31);
+    auto kfrag = [&](int key, int ks) {
+      const int dc = ks * 2 + half;
+      return *reinterpret_cast<const bf16x8_t*>(&Kt[key * HD + ((dc ^ (key % CPR)) << 3)]);
+    };
+    bf16x8_t a0 = kfrag(key0, 0), a1 = kfrag(key1, 0);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int dc = ks * 2 + half;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&Ks[buf * TILE + key * HD + ((dc ^ (key % CPR)) << 3)]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8_t n0 = a0, n1 = a1;
+      if (ks + 1 < NKS) {
+        n0 = kfrag(key0, ks + 1);
+        n1 = kfrag(key1, ks + 1);
       }
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s[1], 0, 0, 0);
+      a0 = n0;
+      a1 = n1;
     }
     // tile max of the raw scores (masked keys -> -inf); the mask is only
     // evaluated on tiles that reach past some column's last visible key
@@ -300,7 +323,6 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
         const int d0 = db * 32 + ((lane >> 4) & 1) * 16;
         const int kx = key_lo + ((lane & 15) >> 2);
         const int dx = d0 + 4 * (lane & 3);
-        const lds_u16_t* vb = ldsV + buf * TILE;
         const v4i16_t lo = lds_read_tr16(vb + kx * HD + (((dx >> 3) ^ vswz(kx)) << 3) + (dx & 7));
         const v4i16_t hi = lds_read_tr16(vb + (kx + 8) * HD + (((dx >> 3) ^ vswz(kx + 8)) << 3) + (dx & 7));
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -310,6 +332,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     }  // wave computes this tile
     wait_loads();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    tile(t, S0{});
+    if (t + 1 < ntiles) tile(t + 1, S1{});
   }
   wait_loads();     // own K/V (when no key tile was streamed)
   __syncthreads();
@@ -350,8 +376,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
 #pragma unroll
         for (int j = 0; j < 4; ++j) oacc[db][i4 * 4 + j] = __builtin_fmaf(ps, v4[j], oacc[db][i4 * 4 + j]);
       }
-    // normalised output of this column into the tile region, column layout
-    // with the query block's chunk swizzle
+  }
+  __syncthreads();  // every wave is done with the own K and V in the query block
+  if (wave_active) {
+    // normalised output of this column into the query block, column layout
+    // with its chunk swizzle
     if (qvalid) {
       const float ltot = lsum + __shfl_xor(lsum, 32, 64);
       const float inv = 1.0f / ltot;
@@ -362,7 +391,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
           uint2 o;
           o.x = pack_bf16x2(oacc[db][i4 * 4 + 0] * inv, oacc[db][i4 * 4 + 1] * inv);
           o.y = pack_bf16x2(oacc[db][i4 * 4 + 2] * inv, oacc[db][i4 * 4 + 3] * inv);
-          *reinterpret_cast<uint2*>(&smem[qc * HD + (((db * 4 + i4) ^ cswz(qc)) << 3) + half * 4]) = o;
+          *reinterpret_cast<uint2*>(&Qs[qc * HD + (((db * 4 + i4) ^ cswz(qc)) << 3) + half * 4]) = o;
         }
     }
   }
@@ -375,7 +404,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     const int col = c / CPR, slot = c % CPR;
     const int lr = col / G;
     if (lr < item_nrows) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&smem[c * 8]);
+      const uint4 v = *reinterpret_cast<const uint4*>(&Qs[c * 8]);
       *reinterpret_cast<uint4*>(obase + (size_t)lr * ldo + (col % G) * HD + ((slot ^ cswz(col)) << 3)) = v;
     }
   }
