@@ -95,9 +95,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t Qs[NC * HD];
 
-  const int n_items = BRANCH ? b.hdr->n_bitems : b.hdr->n_pitems;
-  if ((int)blockIdx.x >= n_items) return;
+  // the item and the item count load together (the grid never exceeds the
+  // item buffer, so the read is in bounds even for surplus blocks; testing
+  // one of its fields in the exit condition keeps its load above the branch)
   const WorkItem item = (BRANCH ? b.bitems : b.pitems)[blockIdx.x];
+  const int n_items = BRANCH ? b.hdr->n_bitems : b.hdr->n_pitems;
+  if ((int)blockIdx.x >= n_items || item.L < 1) return;
   struct {
     int row_off, L, K;
   } const sd = {item.row_off, item.L, item.K};
@@ -217,9 +220,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   __syncthreads();  // every wave holds its query fragments; the block is free
 
   // The rows' own K and V into the query block: own-K row r at [r HD], own-V
-  // row r at [(rows_per_item + r) HD], chunk k at slot k ^ (r % CPR).  In
-  // flight while the first key tile is multiplied.
-  {
+  // row r at [(rows_per_item + r) HD], chunk k at slot k ^ (r % CPR).  Issued
+  // once the first key tile's QK product is under way, so they fly while that
+  // tile is finished.
+  auto issue_own = [&]() {
     const int sin = QCH / (64 * G);  // load instructions per matrix
     for (int ins = wave; ins < 2 * sin; ins += NW) {
       const bool isv = ins >= sin;
@@ -229,18 +233,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
       const uint16_t* src = seq_base + (size_t)(item_row0 + lr) * ld + (isv ? vcol : kcol) + ((slot ^ cswz(r)) << 3);
       load_lds16(src, ldsQ + (isv ? rows_per_item * HD : 0) + (c - lane) * 8);
     }
-  }
+  };
 
   auto tile = [&](int t, auto st) {
     constexpr int ST = decltype(st)::value;
     const int k0 = t * BKV;
-    if (t + 1 < ntiles) issue(k0 + BKV, std::integral_constant<int, ST ^ 1>{});
     const uint16_t* const Kt = kt(st);
     const lds_u16_t* const vb = (const lds_u16_t*)(lds_void_t*)vt(st);
-    if (wave_active && k0 <= wave_klim) {
+    const bool busy = wave_active && k0 <= wave_klim;
+    f32x16_t s[2];
+    if (busy) {
     // S^T for two 32-key blocks, the two accumulation chains interleaved and
     // each k-step's key fragments read one step ahead
-    f32x16_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -263,6 +267,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
       a0 = n0;
       a1 = n1;
     }
+    }  // QK of this tile
+    // the next tile's K and V (and, on the first tile, the rows' own K and V)
+    // go out while the QK products drain
+    if (t + 1 < ntiles) issue(k0 + BKV, std::integral_constant<int, ST ^ 1>{});
+    if (t == 0) issue_own();
+    if (busy) {
     // tile max of the raw scores (masked keys -> -inf); the mask is only
     // evaluated on tiles that reach past some column's last visible key
     float tmax = -INFINITY;
@@ -337,7 +347,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     tile(t, S0{});
     if (t + 1 < ntiles) tile(t + 1, S1{});
   }
-  wait_loads();     // own K/V (when no key tile was streamed)
+  if (ntiles == 0) issue_own();
+  wait_loads();
   __syncthreads();
 
   if (wave_active) {
