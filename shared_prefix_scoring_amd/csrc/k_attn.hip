@@ -30,7 +30,9 @@ namespace {
 #ifndef ATTN_NW
 #define ATTN_NW 8
 #endif
-constexpr int BKV = 64;        // keys per tile
+#ifndef ATTN_BKV
+#define ATTN_BKV 64
+#endif
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
@@ -69,7 +71,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // exceeds it by more than that.
 constexpr float kLazyTau = 8.0f;
 
-template <int HD, int NW>
+template <int HD, int NW, int BKV>
 __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ QKV, int ld,
                                                  uint16_t* __restrict__ O, int ldo, DevBatch b, int H,
                                                  int Hkv, float scale_log2, int branch) {
@@ -79,6 +81,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   constexpr int CPR = HD / 8;          // 16-byte chunks per key row / per query column
   constexpr int NC = NW * 32;          // query columns per workgroup
   constexpr int TILE = BKV * HD;       // elements of one K or V tile
+  constexpr int KB = BKV / 32;         // 32-key blocks per tile
+  static_assert(BKV == 32 || BKV == 64, "key tile");
   constexpr int QCH = NC * CPR;        // 16-byte chunks of the query block
   static_assert(QCH % (64 * NW) == 0, "staging layout");
   auto vswz = [](int key) { return vswz_t<CPR>(key); };
@@ -241,31 +245,31 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     const uint16_t* const Kt = kt(st);
     const lds_u16_t* const vb = (const lds_u16_t*)(lds_void_t*)vt(st);
     const bool busy = wave_active && k0 <= wave_klim;
-    f32x16_t s[2];
+    f32x16_t s[KB];
     if (busy) {
-    // S^T for two 32-key blocks, the two accumulation chains interleaved and
-    // each k-step's key fragments read one step ahead
+    // S^T for the tile's 32-key blocks, their accumulation chains interleaved
+    // and each k-step's key fragments read one step ahead
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-    const int key0 = lane & 31, key1 = 32 + (lane & 31);
-    auto kfrag = [&](int key, int ks) {
+    auto kfrag = [&](int kb, int ks) {
+      const int key = kb * 32 + (lane & 31);
       const int dc = ks * 2 + half;
       return *reinterpret_cast<const bf16x8_t*>(&Kt[key * HD + ((dc ^ (key % CPR)) << 3)]);
     };
-    bf16x8_t a0 = kfrag(key0, 0), a1 = kfrag(key1, 0);
+    bf16x8_t a[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) a[kb] = kfrag(kb, 0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8_t n0 = a0, n1 = a1;
-      if (ks + 1 < NKS) {
-        n0 = kfrag(key0, ks + 1);
-        n1 = kfrag(key1, ks + 1);
-      }
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s[0], 0, 0, 0);
-      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s[1], 0, 0, 0);
-      a0 = n0;
-      a1 = n1;
+      bf16x8_t n[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) n[kb] = ks + 1 < NKS ? kfrag(kb, ks + 1) : a[kb];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[ks], s[kb], 0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) a[kb] = n[kb];
     }
     }  // QK of this tile
     // the next tile's K and V (and, on the first tile, the rows' own K and V)
@@ -278,12 +282,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     float tmax = -INFINITY;
     if (k0 + BKV - 1 <= wave_kmin) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
     } else {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     const float msafe = m == -INFINITY ? 0.f : m;
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -msafe));
@@ -318,9 +322,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
       }
     lsum += psum;
 
-    // O^T += V^T P^T over 4 k-steps of 16 keys
+    // O^T += V^T P^T over the tile's k-steps of 16 keys
 #pragma unroll
-    for (int ks2 = 0; ks2 < 4; ++ks2) {
+    for (int ks2 = 0; ks2 < BKV / 16; ++ks2) {
       const int kb = ks2 >> 1, rb = (ks2 & 1) * 8;
       bf16x8_t pb;
 #pragma unroll
@@ -421,13 +425,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   }
 }
 
-constexpr int NW = ATTN_NW;  // query columns per workgroup = 32 NW
+constexpr int NW = ATTN_NW;    // query columns per workgroup = 32 NW
+constexpr int BKV = ATTN_BKV;  // keys per streamed tile
 
 template <int HD>
 void launch_hd(hipStream_t s, bool branch, int cap_items, const uint16_t* QKV, int ld, uint16_t* O, int ldo,
                DevBatch b, int H, int Hkv, float scale_log2) {
   const dim3 grid(cap_items, Hkv);
-  hipLaunchKernelGGL((k_attn<HD, NW>), grid, dim3(NW * 64), 0, s, QKV, ld, O, ldo, b, H, Hkv, scale_log2,
+  hipLaunchKernelGGL((k_attn<HD, NW, BKV>), grid, dim3(NW * 64), 0, s, QKV, ld, O, ldo, b, H, Hkv, scale_log2,
                      branch ? 1 : 0);
 }
 
