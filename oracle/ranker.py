@@ -220,59 +220,73 @@ def score_head(model: OracleModel, h: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 
-def tree_mask(L: int, K: int) -> np.ndarray:
-    """Visibility over [prefix (L rows); K candidate rows].
+def tree_mask(L: int, K: int, m: int = 1) -> np.ndarray:
+    """Visibility over [prefix (L rows); K candidate branches of m rows each].
 
-    Prefix row t sees prefix rows 0..t.  Candidate j sees the whole prefix and
-    itself, never another candidate ([digest] 核心方法; [mindverse]
-    "Gemeinsame Nutzerhistorie, getrennte Kandidatenzweige").
+    Prefix row t sees prefix rows 0..t.  Row i of candidate branch j sees the
+    whole prefix and rows 0..i of its own branch, never another candidate
+    ([digest] 核心方法; [mindverse] "Gemeinsame Nutzerhistorie, getrennte
+    Kandidatenzweige").  m = 1 is the one-vector item of the pages' main
+    setting; m > 1 is an item spread over m vectors (the pages' FIR m = 8
+    rating service, [digest] 实验结果; [digest] 未来方向 (2)), read here as a
+    causal branch.
     """
-    n = L + K
+    n = L + K * m
     allowed = np.zeros((n, n), dtype=bool)
     for t in range(L):
         allowed[t, : t + 1] = True
     for j in range(K):
-        allowed[L + j, :L] = True
-        allowed[L + j, L + j] = True
+        b = L + j * m
+        for i in range(m):
+            allowed[b + i, :L] = True
+            allowed[b + i, b:b + i + 1] = True
     return allowed
 
 
-def mis_positions(L: int, K: int) -> np.ndarray:
-    """Prefix rows at 0..L-1; every candidate at logical position L ([digest] 方法步骤详情 step 4)."""
-    return np.concatenate([np.arange(L), np.full(K, L)]).astype(np.int64)
+def mis_positions(L: int, K: int, m: int = 1) -> np.ndarray:
+    """Prefix rows at 0..L-1; row i of every candidate branch at logical
+    position L + i, where a lone candidate appended to the prefix would sit
+    ([digest] 方法步骤详情 step 4)."""
+    return np.concatenate([np.arange(L), np.tile(L + np.arange(m), K)]).astype(np.int64)
 
 
 def oracle_mis(model: OracleModel, prefix: Sequence[int], cands: Sequence[int],
-               pos_offset: int = 0) -> np.ndarray:
-    """Scores of the K candidates, in input order, from one packed MIS forward."""
+               pos_offset: int = 0, m: int = 1) -> np.ndarray:
+    """Scores of the K candidates, in input order, from one packed MIS forward.
+
+    `cands` holds K*m ids, candidate-major; a candidate is scored at the last
+    row of its branch ([digest] 核心方法: the last hidden state)."""
     prefix = np.asarray(prefix, dtype=np.int64)
     cands = np.asarray(cands, dtype=np.int64)
-    L, K = prefix.shape[0], cands.shape[0]
-    if L < 1 or K < 1:
-        raise ValueError("need L >= 1 and K >= 1")
+    L = prefix.shape[0]
+    if L < 1 or m < 1 or cands.shape[0] < m or cands.shape[0] % m:
+        raise ValueError("need L >= 1, m >= 1 and K*m candidate ids with K >= 1")
+    K = cands.shape[0] // m
     x = embed_rows(model, np.concatenate([prefix, cands]))
-    pos = mis_positions(L, K) + pos_offset
-    h = decoder_forward(model, x, pos, tree_mask(L, K))
-    return score_head(model, h[L:])
+    pos = mis_positions(L, K, m) + pos_offset
+    h = decoder_forward(model, x, pos, tree_mask(L, K, m))
+    return score_head(model, h[L + m - 1::m])
 
 
 def oracle_mis_packed(model: OracleModel, requests: Sequence[tuple]) -> List[np.ndarray]:
     """Several requests packed one after another in a single forward.
 
-    The mask is block-diagonal over requests (a request never sees another) with
-    each block the request's tree mask; positions restart at 0 per request.
+    A request is (prefix, cands) or (prefix, cands, m).  The mask is
+    block-diagonal over requests (a request never sees another) with each
+    block the request's tree mask; positions restart at 0 per request.
     """
     ids, pos, blocks, spans = [], [], [], []
     row = 0
-    for prefix, cands in requests:
-        prefix = np.asarray(prefix, dtype=np.int64)
-        cands = np.asarray(cands, dtype=np.int64)
-        L, K = prefix.shape[0], cands.shape[0]
+    for req in requests:
+        prefix = np.asarray(req[0], dtype=np.int64)
+        cands = np.asarray(req[1], dtype=np.int64)
+        m = req[2] if len(req) > 2 else 1
+        L, K = prefix.shape[0], cands.shape[0] // m
         ids.append(np.concatenate([prefix, cands]))
-        pos.append(mis_positions(L, K))
-        blocks.append(tree_mask(L, K))
-        spans.append((row + L, row + L + K))
-        row += L + K
+        pos.append(mis_positions(L, K, m))
+        blocks.append(tree_mask(L, K, m))
+        spans.append((row + L + m - 1, row + L + K * m, m))
+        row += L + K * m
     allowed = np.zeros((row, row), dtype=bool)
     r = 0
     for b in blocks:
@@ -280,23 +294,23 @@ def oracle_mis_packed(model: OracleModel, requests: Sequence[tuple]) -> List[np.
         r += b.shape[0]
     x = embed_rows(model, np.concatenate(ids))
     h = decoder_forward(model, x, np.concatenate(pos), allowed)
-    return [score_head(model, h[a:b]) for a, b in spans]
+    return [score_head(model, h[a:b:m]) for a, b, m in spans]
 
 
 def brute_force_independent(model: OracleModel, prefix: Sequence[int], cands: Sequence[int],
-                            which: Sequence[int] | None = None) -> np.ndarray:
+                            which: Sequence[int] | None = None, m: int = 1) -> np.ndarray:
     """The definition, literally: for each candidate, a full causal forward over
-    [prefix; c_j] at positions 0..L, scored at the last row.  `which` limits the
-    candidates evaluated (all by default)."""
+    [prefix; its m ids] at positions 0..L+m-1, scored at the last row.  `which`
+    limits the candidates evaluated (all by default)."""
     prefix = np.asarray(prefix, dtype=np.int64)
     cands = np.asarray(cands, dtype=np.int64)
     L = prefix.shape[0]
-    idx = range(cands.shape[0]) if which is None else which
-    causal = np.tril(np.ones((L + 1, L + 1), dtype=bool))
-    pos = np.arange(L + 1)
+    idx = range(cands.shape[0] // m) if which is None else which
+    causal = np.tril(np.ones((L + m, L + m), dtype=bool))
+    pos = np.arange(L + m)
     out = []
     for j in idx:
-        x = embed_rows(model, np.concatenate([prefix, cands[j:j + 1]]))
+        x = embed_rows(model, np.concatenate([prefix, cands[j * m:(j + 1) * m]]))
         h = decoder_forward(model, x, pos, causal)
         out.append(score_head(model, h[-1:])[0])
     return np.array(out, dtype=F64)
@@ -337,9 +351,9 @@ def decode_incremental(model: OracleModel, ids: Sequence[int]) -> float:
     return float(score_head(model, h[None])[0])
 
 
-def pair_count(L: int, K: int) -> Dict[str, int]:
+def pair_count(L: int, K: int, m: int = 1) -> Dict[str, int]:
     """Allowed (query, key) pairs per layer: MIS tree mask versus K independent
-    causal sequences of L+1 rows, counted from the masks themselves."""
-    mis = int(tree_mask(L, K).sum())
-    one = int(np.tril(np.ones((L + 1, L + 1), dtype=bool)).sum())
+    causal sequences of L+m rows, counted from the masks themselves."""
+    mis = int(tree_mask(L, K, m).sum())
+    one = int(np.tril(np.ones((L + m, L + m), dtype=bool)).sum())
     return {"mis": mis, "independent": K * one, "eliminated": K * one - mis}

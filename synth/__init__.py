@@ -169,8 +169,9 @@ def make_vid_table(cfg: ModelConfig, weights: Dict[str, np.ndarray] | None = Non
 
 @dataclasses.dataclass
 class Request:
-    prefix: np.ndarray      # int32 [L]: instruction, then (marker, VID, feedback...) per item
-    cands: np.ndarray       # int32 [K]: candidate VIDs (V + row)
+    prefix: np.ndarray      # int32 [L]: instruction, then (marker, VID x m, feedback...) per item
+    cands: np.ndarray       # int32 [K*m]: candidate VIDs (V + row), m per candidate, candidate-major
+    m: int = 1              # item vectors per item (history and candidates)
 
     @property
     def L(self) -> int:
@@ -178,7 +179,7 @@ class Request:
 
     @property
     def K(self) -> int:
-        return int(self.cands.shape[0])
+        return int(self.cands.shape[0]) // self.m
 
 
 @dataclasses.dataclass(frozen=True)
@@ -193,6 +194,8 @@ class Workload:
     feedback: object
     n_cand: int
     cycle_items: bool = False
+    m: int = 1                          # item vectors per item
+    cand_cycle: Tuple[int, ...] = ()    # if set, candidate counts cycled per request
 
 
 WORKLOADS = {
@@ -201,6 +204,10 @@ WORKLOADS = {
     3: Workload("0.6b-C64-K100-varlen", 10_000, 32, (1, 3, 5, 10), ("poisson", 40, 5, 120), 100),
     4: Workload("0.6b-C8-K8-rating", 256, 32, (1, 3, 5, 10), 20, 8, cycle_items=True),
     5: Workload("0.6b-C16-L4096-K512", 16, 16, (60,), 66, 512),
+    # items spread over m = 8 vectors, candidate counts cycled over {5, 20, 50, 100}:
+    # the shape of the pages' FIR m = 8 rating service ([digest] 实验结果)
+    6: Workload("0.6b-C8-m8-rating", 256, 32, (1, 3, 5, 10), 20, 100, cycle_items=True, m=8,
+                cand_cycle=(5, 20, 50, 100)),
 }
 
 
@@ -212,31 +219,39 @@ def _template(cfg: ModelConfig, seed: int, n_instr: int):
 
 
 def make_requests(config_id: int, cfg: ModelConfig, n_requests: int | None = None,
-                  seed: int | None = None, n_cand: int | None = None) -> List[Request]:
-    """Synthetic requests for workload `config_id` (1..5).
+                  seed: int | None = None, n_cand: int | None = None, m: int | None = None) -> List[Request]:
+    """Synthetic requests for workload `config_id` (1..6).
 
     Shared per run: one marker token id and one instruction of n_instr token ids.
-    Per request: n history items, each [marker, V + iota, f feedback ids] with
-    iota drawn without replacement from the table and feedback ids uniform in
-    [0, vocab); then K candidate VIDs drawn without replacement from the rows
-    not in the history (target first, then random negatives).
+    Per request: n history items, each [marker, m VIDs, f feedback ids] with
+    the VIDs drawn without replacement from the table and feedback ids uniform
+    in [0, vocab); then K candidates of m VIDs each, drawn without replacement
+    from the rows not in the history (target first, then random negatives).
+    m = 1 (one vector per item) unless the workload or the caller says
+    otherwise.
     """
     wl = WORKLOADS[config_id]
     seed = config_id if seed is None else seed
     n_req = wl.n_requests if n_requests is None else n_requests
-    k = wl.n_cand if n_cand is None else n_cand
+    m = wl.m if m is None else m
     marker, instr = _template(cfg, seed, wl.n_instr)
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
     V, N = cfg.vocab, cfg.n_vid
     reqs: List[Request] = []
     for r in range(n_req):
+        if n_cand is not None:
+            k = n_cand
+        elif wl.cand_cycle:
+            k = wl.cand_cycle[r % len(wl.cand_cycle)]
+        else:
+            k = wl.n_cand
         if wl.cycle_items:
             n = wl.n_items[r % len(wl.n_items)]
         else:
             n = int(wl.n_items[int(rng.integers(0, len(wl.n_items)))])
         # history rows and candidate rows: distinct, candidates exclude history
-        rows = _distinct(rng, N, n + k)
-        hist, cand = rows[:n], rows[n:]
+        rows = _distinct(rng, N, (n + k) * m)
+        hist, cand = rows[:n * m], rows[n * m:]
         parts = [instr]
         for i in range(n):
             if isinstance(wl.feedback, tuple):
@@ -245,10 +260,10 @@ def make_requests(config_id: int, cfg: ModelConfig, n_requests: int | None = Non
             else:
                 f = int(wl.feedback)
             fb = rng.integers(0, V, size=f).astype(np.int32)
-            parts.append(np.array([marker, V + hist[i]], dtype=np.int32))
+            parts.append(np.concatenate([[marker], V + hist[i * m:(i + 1) * m]]).astype(np.int32))
             parts.append(fb)
         prefix = np.concatenate(parts).astype(np.int32)
-        reqs.append(Request(prefix=prefix, cands=(V + cand).astype(np.int32)))
+        reqs.append(Request(prefix=prefix, cands=(V + cand).astype(np.int32), m=m))
     return reqs
 
 
@@ -277,8 +292,9 @@ def poisson_arrivals(n: int, rate_per_s: float, seed: int) -> np.ndarray:
 def pack_ids(reqs: List[Request]) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Concatenate requests as [prefix_0, cands_0, prefix_1, cands_1, ...].
 
-    Returns (ids int32 [sum(L+K)], prefix_len int32 [C], n_cand int32 [C]).
-    This is the id layout the library's device entry point consumes.
+    Returns (ids int32 [sum(L+K*m)], prefix_len int32 [C], n_cand int32 [C]).
+    This is the id layout the library's device entry point consumes (with
+    each request's m passed alongside when it is not 1).
     """
     ids = np.concatenate([np.concatenate([r.prefix, r.cands]) for r in reqs]).astype(np.int32)
     return ids, np.array([r.L for r in reqs], np.int32), np.array([r.K for r in reqs], np.int32)

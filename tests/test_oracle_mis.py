@@ -138,3 +138,70 @@ def test_identity_qwen_shape(qwen):
     ind = brute_force_independent(model, req.prefix, req.cands, which=which)
     assert rel_err(mis[which], ind) < 1e-10
     assert np.all(np.isfinite(mis)) and np.std(mis) > 1e-2
+
+
+# ---------------------------------------------------------------------------
+# multi-vector items: a candidate spans m rows at positions L..L+m-1, causal
+# inside its own branch, scored at its last row
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("m", [2, 3])
+def test_multivector_identity_tiny(tiny, m):
+    # packed MIS with m-row branches equals appending each candidate's m ids alone
+    cfg, _, _, model = tiny
+    (req,) = synth.make_requests(1, cfg, m=m)
+    assert req.m == m and req.K == 8 and req.cands.shape[0] == 8 * m
+    mis = oracle_mis(model, req.prefix, req.cands, m=m)
+    ind = brute_force_independent(model, req.prefix, req.cands, m=m)
+    assert mis.shape == (8,)
+    assert rel_err(mis, ind) < 1e-12
+    assert np.std(mis) > 1e-3
+
+
+def test_multivector_k1_equals_incremental_decoding(tiny):
+    # one candidate of m ids: the packed forward is a plain causal LM over L+m tokens
+    cfg, _, _, model = tiny
+    (req,) = synth.make_requests(1, cfg, m=3, n_cand=1)
+    s = oracle_mis(model, req.prefix, req.cands, m=3)[0]
+    d = decode_incremental(model, np.concatenate([req.prefix, req.cands]))
+    assert abs(s - d) <= 1e-12 * max(1.0, abs(d))
+
+
+@pytest.mark.parametrize("L,K,m", [(48, 8, 2), (452, 100, 8), (7, 1, 5), (13, 9, 3)])
+def test_multivector_pair_counts(L, K, m):
+    # per candidate, the independent sequence holds L(L+1)/2 prefix pairs plus the
+    # branch's own pairs; MIS keeps one copy of the prefix: (K-1) L (L+1) / 2 removed
+    pc = pair_count(L, K, m)
+    assert pc["eliminated"] == (K - 1) * L * (L + 1) // 2
+    assert pc["mis"] == L * (L + 1) // 2 + K * (m * L + m * (m + 1) // 2)
+
+
+def test_multivector_mask_and_positions():
+    from oracle.ranker import mis_positions
+    L, K, m = 5, 3, 4
+    mask = tree_mask(L, K, m)
+    pos = mis_positions(L, K, m)
+    assert list(pos[:L]) == list(range(L))
+    for j in range(K):
+        for i in range(m):
+            r = L + j * m + i
+            assert pos[r] == L + i
+            assert mask[r, :L].all()
+            assert mask[r, L:].sum() == i + 1                      # own branch rows 0..i only
+            assert mask[r, L + j * m:L + j * m + i + 1].all()
+    assert np.array_equal(tree_mask(L, K, 1), tree_mask(L, K))
+
+
+def test_multivector_permutation_and_packing(tiny):
+    cfg, _, _, model = tiny
+    (req,) = synth.make_requests(1, cfg, m=2, n_cand=5)
+    base = oracle_mis(model, req.prefix, req.cands, m=2)
+    perm = np.array([3, 0, 4, 1, 2])
+    blocks = req.cands.reshape(5, 2)[perm].reshape(-1)
+    assert np.allclose(oracle_mis(model, req.prefix, blocks, m=2), base[perm], rtol=0, atol=1e-12)
+    # a packed batch mixing m = 2 and m = 1 requests equals per-request scoring
+    (other,) = synth.make_requests(1, cfg, n_cand=3, seed=5)
+    packed = oracle_mis_packed(model, [(req.prefix, req.cands, 2), (other.prefix, other.cands)])
+    assert rel_err(packed[0], base) < 1e-12
+    assert rel_err(packed[1], oracle_mis(model, other.prefix, other.cands)) < 1e-12
