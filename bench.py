@@ -174,6 +174,51 @@ def bench_latency(ranker, cfg, calls):
     return res
 
 
+def bench_multivec(ranker, cfg, rounds):
+    """Items of m = 8 vectors (every history item and candidate spans 8 VID
+    rows; a candidate is an 8-row causal branch), candidate counts cycled over
+    {5, 20, 50, 100}: 256 requests as calls of C = 8 and of C = 1."""
+    import torch
+    import synth
+    reqs = synth.make_requests(6, cfg)
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {"m": 8, "requests": len(reqs)}
+    for C in (1, 8):
+        calls = []
+        for i in range(0, len(reqs), C):
+            b = reqs[i:i + C]
+            ids, L, K = synth.pack_ids(b)
+            calls.append((torch.from_numpy(ids).cuda(), L, K, torch.empty(int(K.sum()), device="cuda"),
+                          max(r.K for r in b)))
+
+        def run(x):
+            ranker.score_dev(x[1], x[2], x[0].data_ptr(), x[3].data_ptr(), use_graph=True, stream=stream,
+                             cand_len=8)
+
+        for x in calls:
+            run(x)
+        torch.cuda.synchronize()
+        lat, lat100 = [], []
+        t0 = time.perf_counter()
+        for _ in range(rounds):
+            for x in calls:
+                t1 = time.perf_counter()
+                run(x)
+                torch.cuda.synchronize()
+                dt = (time.perf_counter() - t1) * 1e3
+                lat.append(dt)
+                if C == 1 and x[4] == 100:
+                    lat100.append(dt)
+        wall = time.perf_counter() - t0
+        n_scores = sum(int(x[2].sum()) for x in calls) * rounds
+        res[f"C{C}"] = {"requests_per_s": round(len(reqs) * rounds / wall, 1),
+                        "scores_per_s": round(n_scores / wall, 1),
+                        "call_p50_ms": round(float(np.median(lat)), 3)}
+        if lat100:
+            res[f"C{C}"]["p50_ms_N100"] = round(float(np.median(lat100)), 3)
+    return res
+
+
 def bench_stress(ranker, cfg, n_req, n_ind):
     """L=4096, K=512: MIS over n_req requests in one call, against independent
     scoring (prefix replicated per candidate, full causal forward) of the
@@ -302,10 +347,11 @@ def main():
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
     ap.add_argument("--summarize-traffic", metavar="DIR",
                     help="write profiles/traffic_gemm_gateup.json from the counter runs under DIR (no GPU)")
-    ap.add_argument("--workload", choices=["headline", "latency", "rating", "stress"], default="headline",
+    ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress"],
+                    default="headline",
                     help="headline: C=64 x K=100 (the metric); latency: one L=452 x K=100 request per call; "
-                         "rating: K=8 at C=8, graph vs eager and ids vs inline vectors; stress: L=4096 x K=512, "
-                         "MIS vs independent")
+                         "rating: K=8 at C=8, graph vs eager and ids vs inline vectors; multivec: items of 8 "
+                         "vectors, K in {5,20,50,100}, C=1 and C=8; stress: L=4096 x K=512, MIS vs independent")
     args = ap.parse_args()
 
     if args.summarize_traffic:
@@ -344,6 +390,8 @@ def main():
             res = bench_rating(ranker, cfg, D, C=8, rounds=5)
         elif args.workload == "latency":
             res = bench_latency(ranker, cfg, calls=100)
+        elif args.workload == "multivec":
+            res = bench_multivec(ranker, cfg, rounds=3)
         else:
             res = bench_stress(ranker, cfg, n_req=16, n_ind=32)
         print(json.dumps({"workload": args.workload, **res}), flush=True)

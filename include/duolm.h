@@ -97,14 +97,23 @@ int duolm_get_dims(const duolm_ranker* r, duolm_dims* out);
  * throughput).  When non-NULL it holds one fp16 row of d_model values for
  * every position whose id is >= V, in prefix-then-candidates order, and
  * those ids only mark the positions (any value >= V); no table is needed.
+ *
+ * cand_len (optional, 0 means 1): ids per candidate.  An item spread over m
+ * vectors (the pages' FIR m = 8 rating service, [digest] 实验结果; 未来方向
+ * (2)) is a candidate branch of m rows at logical positions L .. L + m - 1,
+ * causal inside the branch and blind to other candidates; it is scored at
+ * its last row.  cand_ids then holds n_cand * cand_len ids, candidate-major.
  */
 typedef struct {
   const int32_t* ids;          /* prefix_len ids, each in [0, V + N) (or >= V with inline_vecs) */
   int32_t prefix_len;          /* L >= 1 */
-  const int32_t* cand_ids;     /* n_cand ids in [0, V + N) (VIDs in practice) */
-  int32_t n_cand;              /* K >= 1 */
+  const int32_t* cand_ids;     /* n_cand * max(cand_len, 1) ids in [0, V + N) (VIDs in practice) */
+  int32_t n_cand;              /* K >= 1 candidates */
   const uint16_t* inline_vecs; /* NULL, or fp16 [number of ids >= V][d_model] */
+  int32_t cand_len;            /* m: 0 or 1 (one row per candidate), up to DUOLM_MAX_CAND_LEN */
 } duolm_request;
+
+#define DUOLM_MAX_CAND_LEN 64
 
 typedef enum {
   DUOLM_MODE_MIS = 0,        /* packed: prefix once, K one-row branches under the tree mask */
@@ -123,8 +132,10 @@ typedef struct {
  *   scores      : host buffer of sum(n_cand) floats, written request-major,
  *                 candidates in input order (digest, 方法步骤详情 step 4).
  *   opts        : NULL means MIS with graph replay on the handle's stream.
- * Ids are validated on the host before any device work.
- * Errors: EINVAL, ERANGE, ESTATE (a VID id with no table loaded), ENOMEM, EHIP.
+ * Ids are validated on the host before any device work.  In independent
+ * mode a candidate of m ids is appended alone to its prefix as m causal rows.
+ * Errors: EINVAL (also cand_len outside [0, DUOLM_MAX_CAND_LEN]), ERANGE,
+ * ESTATE (a VID id with no table loaded), ENOMEM, EHIP.
  */
 int duolm_score_batch(duolm_ranker* r, const duolm_request* reqs, int32_t n_req, float* scores,
                       const duolm_opts* opts);
@@ -133,14 +144,17 @@ int duolm_score_batch(duolm_ranker* r, const duolm_request* reqs, int32_t n_req,
  * Device-resident variant: the ids are already in device memory (item
  * vectors always come from the table here).
  *   prefix_len, n_cand : host arrays of n_req lengths.
+ *   cand_len           : host array of n_req ids-per-candidate (as in
+ *                        duolm_request), or NULL for one id per candidate.
  *   d_ids              : device, int32, the requests concatenated as
  *                        [prefix_0, cands_0, prefix_1, cands_1, ...].
  *   d_scores           : device, sum(n_cand) floats, request-major.
  * Ids are range-checked on the device: an out-of-range id makes the call
  * return ERANGE with d_scores untouched.
  */
-int duolm_score_batch_dev(duolm_ranker* r, const int32_t* prefix_len, const int32_t* n_cand, int32_t n_req,
-                          const int32_t* d_ids, float* d_scores, const duolm_opts* opts);
+int duolm_score_batch_dev(duolm_ranker* r, const int32_t* prefix_len, const int32_t* n_cand,
+                          const int32_t* cand_len, int32_t n_req, const int32_t* d_ids, float* d_scores,
+                          const duolm_opts* opts);
 
 /* Kernel classes for the profiling counters. */
 typedef enum {

@@ -47,7 +47,7 @@ class duolm_dims(C.Structure):
 class duolm_request(C.Structure):
     _fields_ = [("ids", C.POINTER(C.c_int32)), ("prefix_len", C.c_int32),
                 ("cand_ids", C.POINTER(C.c_int32)), ("n_cand", C.c_int32),
-                ("inline_vecs", C.c_void_p)]
+                ("inline_vecs", C.c_void_p), ("cand_len", C.c_int32)]
 
 
 class duolm_opts(C.Structure):
@@ -67,8 +67,8 @@ EXPORTS = {
     "duolm_get_dims": (C.c_int, [C.c_void_p, C.POINTER(duolm_dims)]),
     "duolm_score_batch": (C.c_int, [C.c_void_p, C.POINTER(duolm_request), C.c_int32, C.c_void_p,
                                     C.POINTER(duolm_opts)]),
-    "duolm_score_batch_dev": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
-                                        C.POINTER(duolm_opts)]),
+    "duolm_score_batch_dev": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                        C.c_void_p, C.POINTER(duolm_opts)]),
     "duolm_set_profiling": (C.c_int, [C.c_void_p, C.c_uint32]),
     "duolm_get_kernel_stats": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(duolm_kernel_stats)]),
     "duolm_last_error": (C.c_char_p, []),
@@ -104,18 +104,37 @@ def _i32(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
 
-def _requests(reqs: Sequence[Tuple]):
+def _cand_lens(n: int, cand_len) -> np.ndarray:
+    """Ids per candidate for each of n requests: None (1), one int, or a sequence."""
+    if cand_len is None:
+        return np.ones(n, dtype=np.int32)
+    if np.isscalar(cand_len):
+        return np.full(n, int(cand_len), dtype=np.int32)
+    m = _i32(cand_len)
+    if m.shape != (n,):
+        raise ValueError("cand_len must have one entry per request")
+    return m
+
+
+def _requests(reqs: Sequence[Tuple], cand_len=None):
     """Requests as (prefix_ids, cand_ids) or (prefix_ids, cand_ids, inline_vecs),
-    inline_vecs an fp16-bits array [number of ids >= V, d_model]."""
+    inline_vecs an fp16-bits array [number of ids >= V, d_model].  cand_len:
+    ids per candidate (None, one int, or one per request); cand_ids then holds
+    n_cand * cand_len ids, candidate-major."""
     keep = []
     arr = (duolm_request * len(reqs))()
+    ms = _cand_lens(len(reqs), cand_len)
     for i, req in enumerate(reqs):
         p, c = _i32(req[0]), _i32(req[1])
+        m = max(int(ms[i]), 1)
+        if c.shape[0] % m:
+            raise ValueError(f"request {i}: {c.shape[0]} candidate ids is not a multiple of cand_len {m}")
         keep += [p, c]
         arr[i].ids = p.ctypes.data_as(C.POINTER(C.c_int32))
         arr[i].prefix_len = p.shape[0]
         arr[i].cand_ids = c.ctypes.data_as(C.POINTER(C.c_int32))
-        arr[i].n_cand = c.shape[0]
+        arr[i].n_cand = c.shape[0] // m
+        arr[i].cand_len = int(ms[i])
         if len(req) > 2 and req[2] is not None:
             v = np.ascontiguousarray(req[2], dtype=np.uint16)
             keep.append(v)
@@ -157,9 +176,10 @@ def duolm_get_dims(r) -> duolm_dims:
     return d
 
 
-def duolm_score_batch(r, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None) -> np.ndarray:
-    arr, keep = _requests(reqs)
-    n = sum(int(np.asarray(r[1]).shape[0]) for r in reqs)
+def duolm_score_batch(r, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None,
+                      cand_len=None) -> np.ndarray:
+    arr, keep = _requests(reqs, cand_len)
+    n = sum(int(arr[i].n_cand) for i in range(len(reqs)))
     out = np.empty(n, dtype=np.float32)
     o = _opts(mode, use_graph, stream)
     _check(lib().duolm_score_batch(r, arr, len(reqs), out.ctypes.data, C.byref(o)))
@@ -168,11 +188,12 @@ def duolm_score_batch(r, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = Tru
 
 
 def duolm_score_batch_dev(r, prefix_len, n_cand, d_ids: int, d_scores: int, mode: int = DUOLM_MODE_MIS,
-                          use_graph: bool = True, stream=None) -> None:
+                          use_graph: bool = True, stream=None, cand_len=None) -> None:
     L, K = _i32(prefix_len), _i32(n_cand)
+    M = None if cand_len is None else _cand_lens(L.shape[0], cand_len)
     o = _opts(mode, use_graph, stream)
-    _check(lib().duolm_score_batch_dev(r, L.ctypes.data, K.ctypes.data, L.shape[0], C.c_void_p(d_ids),
-                                       C.c_void_p(d_scores), C.byref(o)))
+    _check(lib().duolm_score_batch_dev(r, L.ctypes.data, K.ctypes.data, None if M is None else M.ctypes.data,
+                                       L.shape[0], C.c_void_p(d_ids), C.c_void_p(d_scores), C.byref(o)))
 
 
 def duolm_set_profiling(r, class_mask: int) -> None:
@@ -193,8 +214,9 @@ def duolm_free_ranker(r) -> None:
     lib().duolm_free_ranker(r)
 
 
-def duolm_debug_forward(r, reqs, layer: int, stage: int, out: np.ndarray, mode: int = DUOLM_MODE_MIS) -> np.ndarray:
-    arr, keep = _requests(reqs)
+def duolm_debug_forward(r, reqs, layer: int, stage: int, out: np.ndarray, mode: int = DUOLM_MODE_MIS,
+                        cand_len=None) -> np.ndarray:
+    arr, keep = _requests(reqs, cand_len)
     _check(lib().duolm_debug_forward(r, arr, len(reqs), mode, layer, stage, out.ctypes.data, out.nbytes))
     del keep
     return out
@@ -230,19 +252,21 @@ class Ranker:
         duolm_load_vid_table(self.h, rows_fp16)
         self.dims = duolm_get_dims(self.h)
 
-    def score(self, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None) -> np.ndarray:
-        return duolm_score_batch(self.h, reqs, mode, use_graph, stream)
+    def score(self, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None,
+              cand_len=None) -> np.ndarray:
+        return duolm_score_batch(self.h, reqs, mode, use_graph, stream, cand_len)
 
     def score_dev(self, prefix_len, n_cand, d_ids: int, d_scores: int, mode: int = DUOLM_MODE_MIS,
-                  use_graph: bool = True, stream=None) -> None:
-        duolm_score_batch_dev(self.h, prefix_len, n_cand, d_ids, d_scores, mode, use_graph, stream)
+                  use_graph: bool = True, stream=None, cand_len=None) -> None:
+        duolm_score_batch_dev(self.h, prefix_len, n_cand, d_ids, d_scores, mode, use_graph, stream, cand_len)
 
-    def stage(self, reqs, layer: int, stage: str, mode: int = DUOLM_MODE_MIS) -> np.ndarray:
+    def stage(self, reqs, layer: int, stage: str, mode: int = DUOLM_MODE_MIS, cand_len=None) -> np.ndarray:
         d = self.dims
+        ms = [max(int(m), 1) for m in _cand_lens(len(reqs), cand_len)]
         if mode == DUOLM_MODE_MIS:
             T = sum(len(r[0]) + len(r[1]) for r in reqs)
         else:
-            T = sum((len(r[0]) + 1) * len(r[1]) for r in reqs)
+            T = sum((len(r[0]) + m) * (len(r[1]) // m) for r, m in zip(reqs, ms))
         width, dt = {
             "attn_norm": (d.d_model, np.uint16), "mlp_norm": (d.d_model, np.uint16),
             "qkv": ((d.n_heads + 2 * d.n_kv_heads) * d.head_dim, np.uint16),
@@ -250,7 +274,7 @@ class Ranker:
             "attn": (d.n_heads * d.head_dim, np.uint16), "swiglu": (d.d_ffn, np.uint16),
         }.get(stage, (d.d_model, np.float32))
         out = np.empty((T, width), dtype=dt)
-        return duolm_debug_forward(self.h, reqs, layer, STAGES[stage], out, mode)
+        return duolm_debug_forward(self.h, reqs, layer, STAGES[stage], out, mode, cand_len)
 
     def set_profiling(self, classes: Iterable[str]) -> None:
         mask = 0

@@ -460,7 +460,10 @@ DevBatch dev_batch(duolm_ranker* R) {
 // ---------------------------------------------------------------------------
 // planning
 // ---------------------------------------------------------------------------
-void plan_add_seq(duolm_ranker* R, Plan& P, int L, int K, int id_off, int id_len, int cand_id_off, bool head_last) {
+// A sequence: L causal rows, then K candidate branches of M rows each.
+// Branch attention tiles hold whole branches (a branch row's in-branch keys
+// are rows of its own tile); the score head reads each branch's last row.
+void plan_add_seq(duolm_ranker* R, Plan& P, int L, int K, int M, int id_off, int id_len, int cand_id_off) {
   const int G = R->dims.n_heads / R->dims.n_kv_heads;
   const int s = (int)P.seqs.size();
   SeqDesc sd{};
@@ -470,14 +473,16 @@ void plan_add_seq(duolm_ranker* R, Plan& P, int L, int K, int id_off, int id_len
   sd.id_off = id_off;
   sd.id_len = id_len;
   sd.cand_id_off = cand_id_off;
+  sd.M = M;
   P.seqs.push_back(sd);
   P.seq_row_off.push_back(P.T);
-  const int rp = attn_rows_per_item(false, G), rb = attn_rows_per_item(true, G);
-  for (int r0 = 0; r0 < L; r0 += rp) P.pitems.push_back({s, r0, P.T, L, K, {0, 0, 0}});
-  for (int c0 = 0; c0 < K; c0 += rb) P.bitems.push_back({s, c0, P.T, L, K, {0, 0, 0}});
-  if (head_last) P.head_rows.push_back(P.T + L - 1);
-  for (int j = 0; j < K; ++j) P.head_rows.push_back(P.T + L + j);
-  P.T += L + K;
+  const int rp = attn_rows_per_item(false, G);
+  const int rb = attn_rows_per_item(true, G) / M * M;  // whole branches per tile
+  const int KM = K * M;
+  for (int r0 = 0; r0 < L; r0 += rp) P.pitems.push_back({s, r0, P.T, L, KM, M, {0, 0}});
+  for (int c0 = 0; c0 < KM; c0 += rb) P.bitems.push_back({s, c0, P.T, L, KM, M, {0, 0}});
+  for (int j = 0; j < K; ++j) P.head_rows.push_back(P.T + L + j * M + M - 1);
+  P.T += L + KM;
 }
 
 // Close a launch: attention tiles go longest first (their key count is the
@@ -512,11 +517,12 @@ void launch_work(const duolm_ranker* R, const Plan& P, double fl[DUOLM_K_COUNT],
   fl[DUOLM_K_GEMM_DOWN] = 2 * T * F * d;
   by[DUOLM_K_GEMM_DOWN] = (d * F + T * F) * 2 + T * d * 8;
   for (const SeqDesc& s : P.seqs) {
-    const double L = s.L, K = s.K;
+    const double L = s.L, K = s.K, M = s.M;
     fl[DUOLM_K_ATTN_PREFIX] += 4 * hd * H * L * (L + 1) / 2;
     by[DUOLM_K_ATTN_PREFIX] += L * (H * hd * 2 + Hk * hd * 4 + H * hd * 2);
-    fl[DUOLM_K_ATTN_BRANCH] += 4 * hd * H * K * (L + 1);
-    if (K > 0) by[DUOLM_K_ATTN_BRANCH] += L * Hk * hd * 4 + K * (H * hd * 2 + Hk * hd * 4 + H * hd * 2);
+    // branch row i sees L prefix keys and i + 1 keys of its own branch
+    fl[DUOLM_K_ATTN_BRANCH] += 4 * hd * H * K * (M * L + M * (M + 1) / 2);
+    if (K > 0) by[DUOLM_K_ATTN_BRANCH] += L * Hk * hd * 4 + K * M * (H * hd * 2 + Hk * hd * 4 + H * hd * 2);
   }
   by[DUOLM_K_HEAD] = (double)P.head_rows.size() * (d * 4 + 4);
   fl[DUOLM_K_HEAD] = (double)P.head_rows.size() * d * 4;
@@ -721,8 +727,16 @@ int run_launch(duolm_ranker* R, const Plan& P, hipStream_t s, bool use_graph, st
 struct CallInput {
   const int32_t* prefix_len;
   const int32_t* n_cand;
+  const int32_t* cand_len;  // ids (rows) per candidate, per request; null: 1
   int n_req;
 };
+
+int cand_rows(const CallInput& in, int i) { return in.cand_len && in.cand_len[i] > 1 ? in.cand_len[i] : 1; }
+
+// Longest candidate branch the attention tiles take whole.
+int max_cand_len(const duolm_ranker* R) {
+  return std::min(DUOLM_MAX_CAND_LEN, attn_rows_per_item(true, R->dims.n_heads / R->dims.n_kv_heads));
+}
 
 int validate_lengths(duolm_ranker* R, const CallInput& in, int64_t& total_ids, int64_t& total_scores) {
   if (in.n_req < 1) return fail(DUOLM_EINVAL, "n_req must be >= 1");
@@ -730,13 +744,17 @@ int validate_lengths(duolm_ranker* R, const CallInput& in, int64_t& total_ids, i
   total_scores = 0;
   for (int i = 0; i < in.n_req; ++i) {
     const int L = in.prefix_len[i], K = in.n_cand[i];
+    if (in.cand_len && (in.cand_len[i] < 0 || in.cand_len[i] > max_cand_len(R)))
+      return fail(DUOLM_EINVAL, "request %d: cand_len %d outside [0, %d]", i, in.cand_len[i], max_cand_len(R));
+    const int m = cand_rows(in, i);
     if (L < 1) return fail(DUOLM_EINVAL, "request %d: prefix_len %d < 1", i, L);
     if (K < 1) return fail(DUOLM_EINVAL, "request %d: n_cand %d < 1", i, K);
-    if (L > R->dims.max_prefix) return fail(DUOLM_EINVAL, "request %d: prefix_len %d over %d", i, L, R->dims.max_prefix);
-    if ((int64_t)L + K > R->max_rows)
-      return fail(DUOLM_EINVAL, "request %d: L + K = %d over the %lld-row launch limit", i, L + K,
-                  (long long)R->max_rows);
-    total_ids += L + K;
+    if (L + m - 1 > R->dims.max_prefix)
+      return fail(DUOLM_EINVAL, "request %d: prefix_len %d + cand_len %d over %d", i, L, m, R->dims.max_prefix + 1);
+    if ((int64_t)L + (int64_t)K * m > R->max_rows)
+      return fail(DUOLM_EINVAL, "request %d: L + K * cand_len = %lld over the %lld-row launch limit", i,
+                  (long long)L + (long long)K * m, (long long)R->max_rows);
+    total_ids += L + (int64_t)K * m;
     total_scores += K;
   }
   if (total_ids > INT32_MAX / 2) return fail(DUOLM_EINVAL, "batch too large");
@@ -750,26 +768,31 @@ void build_plans(duolm_ranker* R, const CallInput& in, int mode, std::vector<Pla
   int64_t id_off = 0;
   int score = 0;
   for (int i = 0; i < in.n_req; ++i) {
-    const int L = in.prefix_len[i], K = in.n_cand[i];
+    const int L = in.prefix_len[i], K = in.n_cand[i], m = cand_rows(in, i);
     if (mode == DUOLM_MODE_MIS) {
-      if (plans.back().T > 0 && plans.back().T + L + K > R->max_rows) {
+      if (plans.back().T > 0 && plans.back().T + L + (int64_t)K * m > R->max_rows) {
         plan_close(R, plans.back());
         plans.emplace_back();
         plans.back().score_off = score;
       }
-      plan_add_seq(R, plans.back(), L, K, (int)id_off, L, (int)(id_off + L), false);
+      plan_add_seq(R, plans.back(), L, K, m, (int)id_off, L, (int)(id_off + L));
     } else {
+      // Each candidate appended alone to its prefix: a sequence of its own
+      // with the prefix recomputed.  With one candidate the tree mask is the
+      // causal mask over L + m rows, so this is the plain causal forward; its
+      // m rows go through the branch tiles, the same reduction order as in
+      // MIS, which keeps the two modes' scores identical.
       for (int j = 0; j < K; ++j) {
-        if (plans.back().T > 0 && plans.back().T + L + 1 > R->max_rows) {
+        if (plans.back().T > 0 && plans.back().T + L + m > R->max_rows) {
           plan_close(R, plans.back());
           plans.emplace_back();
           plans.back().score_off = score + j;
         }
-        plan_add_seq(R, plans.back(), L + 1, 0, (int)id_off, L, (int)(id_off + L + j), true);
+        plan_add_seq(R, plans.back(), L, 1, m, (int)id_off, L, (int)(id_off + L + (int64_t)j * m));
       }
     }
     score += K;
-    id_off += L + K;
+    id_off += L + (int64_t)K * m;
   }
   plan_close(R, plans.back());
 }
@@ -859,18 +882,23 @@ int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool id
 // that ship their item vectors have each id >= V rewritten to V + N + j, row j
 // of the call's inline table.
 int flatten_requests(const duolm_ranker* R, const duolm_request* reqs, int n_req, std::vector<int32_t>& L,
-                     std::vector<int32_t>& K, std::vector<int32_t>& ids, std::vector<uint16_t>& inl) {
+                     std::vector<int32_t>& K, std::vector<int32_t>& M, std::vector<int32_t>& ids,
+                     std::vector<uint16_t>& inl) {
   if (!reqs || n_req < 1) return fail(DUOLM_EINVAL, "need n_req >= 1 requests");
   L.resize(n_req);
   K.resize(n_req);
+  M.resize(n_req);
   size_t total = 0;
   for (int i = 0; i < n_req; ++i) {
     if (reqs[i].prefix_len < 1 || reqs[i].n_cand < 1)
       return fail(DUOLM_EINVAL, "request %d: prefix_len and n_cand must be >= 1", i);
     if (!reqs[i].ids || !reqs[i].cand_ids) return fail(DUOLM_EINVAL, "request %d: NULL ids", i);
+    if (reqs[i].cand_len < 0 || reqs[i].cand_len > max_cand_len(R))
+      return fail(DUOLM_EINVAL, "request %d: cand_len %d outside [0, %d]", i, reqs[i].cand_len, max_cand_len(R));
     L[i] = reqs[i].prefix_len;
     K[i] = reqs[i].n_cand;
-    total += (size_t)L[i] + K[i];
+    M[i] = reqs[i].cand_len > 1 ? reqs[i].cand_len : 1;
+    total += (size_t)L[i] + (size_t)K[i] * M[i];
   }
   ids.resize(total);
   inl.clear();
@@ -881,8 +909,8 @@ int flatten_requests(const duolm_ranker* R, const duolm_request* reqs, int n_req
     const size_t start = o;
     memcpy(&ids[o], reqs[i].ids, (size_t)L[i] * 4);
     o += L[i];
-    memcpy(&ids[o], reqs[i].cand_ids, (size_t)K[i] * 4);
-    o += K[i];
+    memcpy(&ids[o], reqs[i].cand_ids, (size_t)K[i] * M[i] * 4);
+    o += (size_t)K[i] * M[i];
     if (!reqs[i].inline_vecs) {
       const int64_t lim = (int64_t)V + R->n_vid;
       for (size_t t = start; t < o; ++t) {
@@ -967,18 +995,19 @@ int duolm_get_dims(const duolm_ranker* R, duolm_dims* out) {
 int duolm_score_batch(duolm_ranker* R, const duolm_request* reqs, int32_t n_req, float* scores,
                       const duolm_opts* opts) {
   if (!R || !scores) return fail(DUOLM_EINVAL, "NULL argument");
-  std::vector<int32_t> L, K, ids;
+  std::vector<int32_t> L, K, M, ids;
   std::vector<uint16_t> inl;
-  int rc = flatten_requests(R, reqs, n_req, L, K, ids, inl);
+  int rc = flatten_requests(R, reqs, n_req, L, K, M, ids, inl);
   if (rc) return rc;
-  CallInput in{L.data(), K.data(), n_req};
+  CallInput in{L.data(), K.data(), M.data(), n_req};
   return score_impl(R, in, ids.data(), false, scores, false, opts, inl.data(),
                     (int64_t)(inl.size() / R->dims.d_model));
 }
 
-int duolm_score_batch_dev(duolm_ranker* R, const int32_t* prefix_len, const int32_t* n_cand, int32_t n_req,
-                          const int32_t* d_ids, float* d_scores, const duolm_opts* opts) {
-  CallInput in{prefix_len, n_cand, n_req};
+int duolm_score_batch_dev(duolm_ranker* R, const int32_t* prefix_len, const int32_t* n_cand,
+                          const int32_t* cand_len, int32_t n_req, const int32_t* d_ids, float* d_scores,
+                          const duolm_opts* opts) {
+  CallInput in{prefix_len, n_cand, cand_len, n_req};
   return score_impl(R, in, d_ids, true, d_scores, true, opts);
 }
 
@@ -1033,12 +1062,12 @@ int duolm_debug_forward(duolm_ranker* R, const duolm_request* reqs, int32_t n_re
     return fail(DUOLM_EINVAL, "bad layer/stage");
   if (layer == R->dims.n_layers && stage != DUOLM_STAGE_LAYER_OUT) return fail(DUOLM_EINVAL, "bad stage");
   if (stage == DUOLM_STAGE_EMBED && layer != 0) return fail(DUOLM_EINVAL, "embed stage is layer 0 only");
-  std::vector<int32_t> L, K, ids;
+  std::vector<int32_t> L, K, M, ids;
   std::vector<uint16_t> inl;
-  int rc = flatten_requests(R, reqs, n_req, L, K, ids, inl);
+  int rc = flatten_requests(R, reqs, n_req, L, K, M, ids, inl);
   if (rc) return rc;
   if (!inl.empty()) return fail(DUOLM_EINVAL, "debug forward takes table ids only");
-  CallInput in{L.data(), K.data(), n_req};
+  CallInput in{L.data(), K.data(), M.data(), n_req};
   int64_t total_ids = 0, total_scores = 0;
   if ((rc = validate_lengths(R, in, total_ids, total_scores))) return rc;
   const int64_t lim = (int64_t)R->dims.vocab + R->n_vid;

@@ -12,20 +12,22 @@ namespace duolm {
 // Batch description, uploaded once per forward launch.
 //
 // Rows of the activation buffers are packed sequence by sequence.  A sequence
-// has L causal rows (positions 0..L-1) followed by K one-row candidate
-// branches (all at position L).  MIS: one sequence per request.  Independent
-// scoring: one sequence per (request, candidate) with L = prefix + 1, K = 0.
+// has L causal rows (positions 0..L-1) followed by K candidate branches of M
+// rows each (row i of a branch at position L + i, causal inside its branch).
+// MIS: one sequence per request.  Independent scoring: one sequence per
+// (request, candidate) holding the prefix and that candidate alone (K = 1).
 // Row rho of a sequence takes its id from ids[id_off + rho] when rho < id_len,
 // else from ids[cand_id_off + rho - id_len].
 // ---------------------------------------------------------------------------
 struct SeqDesc {
   int32_t row_off;
   int32_t L;
-  int32_t K;
+  int32_t K;       // candidate branches
   int32_t id_off;
   int32_t id_len;
   int32_t cand_id_off;
-  int32_t pad0, pad1;
+  int32_t M;       // rows per candidate branch (positions L .. L + M - 1)
+  int32_t pad1;
 };
 
 // A tile of query rows: prefix tiles start at row r0 of the sequence,
@@ -33,11 +35,12 @@ struct SeqDesc {
 // workgroup needs one dependent load to start.
 struct WorkItem {
   int32_t seq;
-  int32_t r0;
+  int32_t r0;       // first row: prefix row r0, or branch row r0 (counted from row L; a branch start)
   int32_t row_off;  // the sequence's first row
   int32_t L;
-  int32_t K;
-  int32_t pad[3];
+  int32_t K;        // branch rows of the sequence (candidates x M)
+  int32_t M;        // rows per candidate branch
+  int32_t pad[2];
 };
 
 struct CallHeader {

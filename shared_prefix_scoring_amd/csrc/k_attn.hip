@@ -9,7 +9,10 @@
 //     with Language Models", 核心方法 and 方法步骤详情 step 4).  One workgroup
 //     takes up to 128 candidates x all query heads of one KV head, so each
 //     request's prefix K/V for that head streams from memory once for all of
-//     them; the self term is merged into the online softmax at the end.
+//     them; the self term is merged into the online softmax at the end.  A
+//     candidate spread over M rows (an item of M vectors, same page, 实验结果
+//     FIR m = 8) is a causal branch: row i also merges rows 0..i-1 of its own
+//     branch before its own key.
 //
 // Orientation: each wave computes S^T = K Q^T for 32 query columns (a column
 // is one (row, query head) pair of the KV head's group) with
@@ -114,11 +117,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qc = wave * 32 + (lane & 31);
   const int lrow = qc / G;
-  const int hq = g * G + qc % G;
   const int rows_per_item = NC / G;
+  // Branch tiles hold whole candidate branches of M rows (row i of a branch
+  // sees the prefix and rows 0..i of its own branch).
+  const int M = BRANCH ? item.M : 1;
+  const int rows_used = rows_per_item / M * M;
   // the item's query rows, relative to the sequence start, and how many exist
   const int item_row0 = BRANCH ? sd.L + item.r0 : item.r0;
-  const int item_nrows = min(rows_per_item, (BRANCH ? sd.K : sd.L) - item.r0);
+  const int item_nrows = min(rows_used, (BRANCH ? sd.K : sd.L) - item.r0);
 
   // Every query row sees a run of earlier keys plus its own key.  The earlier
   // keys stream through LDS in 64-key tiles; the row's own (diagonal) key is
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   int kend;     // keys [0, kend) are streamed
   if (BRANCH) {
     const int j = item.r0 + lrow;
-    qvalid = j < sd.K;
+    qvalid = lrow < item_nrows;
     qrel = sd.L + min(j, sd.K - 1);
     klim = sd.L - 1;
     kend = sd.L;
@@ -356,41 +362,50 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   __syncthreads();
 
   if (wave_active) {
-    // diagonal term: the row's own key and value (own-K row lrow of the block)
-    const uint16_t* kself = Qs + lrow * HD;
-    float part = 0.f;
+    // The row's own key and, in a candidate branch, the earlier rows of its
+    // branch: local rows lrow - i .. lrow of the block (i = the row's index
+    // in its branch; tiles start at branch boundaries), merged in order, the
+    // row's own key last.  Every lane runs the branch's M steps; a step past
+    // the row's own key adds a zero weight, leaving the sums unchanged.
+    const int nmerge = BRANCH ? lrow % M + 1 : 1;
+    for (int e = 0; e < M; ++e) {
+      const bool act = e < nmerge;
+      const int kr = act ? lrow - nmerge + 1 + e : lrow;
+      const uint16_t* kself = Qs + kr * HD;
+      float part = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(kself + (((ks * 2 + half) ^ cswz(lrow)) << 3));
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(kself + (((ks * 2 + half) ^ cswz(kr)) << 3));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)qf[ks][e], (float)kv[e], part);
-    }
-    const float dot = part + __shfl_xor(part, 32, 64);
-    const float sv = dot * scale_log2;
-    const bool grow = sv > m + kLazyTau;
-    if (__any(grow)) {
-      const float mnew = grow ? sv : m;
-      const float alpha = grow ? fast_exp2(m - mnew) : 1.0f;
-      lsum *= alpha;
-      m = mnew;
+        for (int e8 = 0; e8 < 8; ++e8) part = __builtin_fmaf((float)qf[ks][e8], (float)kv[e8], part);
+      }
+      const float dot = part + __shfl_xor(part, 32, 64);
+      const float sv = dot * scale_log2;
+      const bool grow = act && sv > m + kLazyTau;
+      if (__any(grow)) {
+        const float mnew = grow ? sv : m;
+        const float alpha = grow ? fast_exp2(m - mnew) : 1.0f;
+        lsum *= alpha;
+        m = mnew;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      const float ps = act ? fast_exp2(sv - m) : 0.f;
+      lsum += half == 0 ? ps : 0.f;
+      const uint16_t* vself = Qs + (rows_per_item + kr) * HD;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const uint2 vv = *reinterpret_cast<const uint2*>(vself + (((db * 4 + i4) ^ cswz(kr)) << 3) + half * 4);
+          const float v4[4] = {bf16_to_f32(vv.x & 0xffffu), bf16_to_f32(vv.x >> 16), bf16_to_f32(vv.y & 0xffffu),
+                               bf16_to_f32(vv.y >> 16)};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) oacc[db][i4 * 4 + j] = __builtin_fmaf(ps, v4[j], oacc[db][i4 * 4 + j]);
+        }
     }
-    const float ps = fast_exp2(sv - m);
-    lsum += half == 0 ? ps : 0.f;
-    const uint16_t* vself = Qs + (rows_per_item + lrow) * HD;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const uint2 vv = *reinterpret_cast<const uint2*>(vself + (((db * 4 + i4) ^ cswz(lrow)) << 3) + half * 4);
-        const float v4[4] = {bf16_to_f32(vv.x & 0xffffu), bf16_to_f32(vv.x >> 16), bf16_to_f32(vv.y & 0xffffu),
-                             bf16_to_f32(vv.y >> 16)};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) oacc[db][i4 * 4 + j] = __builtin_fmaf(ps, v4[j], oacc[db][i4 * 4 + j]);
-      }
   }
   __syncthreads();  // every wave is done with the own K and V in the query block
   if (wave_active) {

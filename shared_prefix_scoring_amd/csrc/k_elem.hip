@@ -13,8 +13,8 @@ namespace duolm {
 // Models", 方法步骤详情 step 3).  Ids V + N + j read row j of the call's
 // inline item vectors (requests that ship vectors instead of ids).  All widen
 // exactly to the fp32 residual stream.  Also writes each row's logical
-// position: causal row rho -> rho, every candidate row -> L (same page,
-// 核心方法 / step 4).
+// position: causal row rho -> rho, row i of every candidate branch -> L + i
+// (same page, 核心方法 / step 4).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, DevBatch b,
                                                const uint16_t* __restrict__ E,
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, 
   const SeqDesc sd = b.seqs[lo];
   const int rho = row - sd.row_off;
   const int id = rho < sd.id_len ? ids[sd.id_off + rho] : ids[sd.cand_id_off + (rho - sd.id_len)];
-  if (lane == 0) pos[row] = rho < sd.L ? rho : sd.L;
+  if (lane == 0) pos[row] = rho < sd.L ? rho : sd.L + (rho - sd.L) % sd.M;
   float* xr = X + (size_t)row * d;
   const int nchunk = d >> 3;  // 8 values per chunk
   if (id < 0 || (int64_t)id >= (int64_t)V + n_vid + b.hdr->n_inline) {

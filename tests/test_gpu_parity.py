@@ -4,7 +4,8 @@ workload shapes: tiny (L=48, K=8), one 0.6B request (L=452, K=100), a packed
 K=8 rating mix, and the L=4096 / K=512 stress shape (checked against GPU
 independent scoring on sampled candidates).  Also: GPU MIS versus GPU
 independent scoring, graph replay versus eager launch, determinism, batch
-and permutation invariance, and the error paths."""
+and permutation invariance, the error paths, and candidates spanning m rows
+(items of m vectors) against the oracle's m-row branches."""
 import numpy as np
 import pytest
 import torch
@@ -262,3 +263,79 @@ def test_graph_replay_after_buffer_growth(gpu_qwen):
     big = reqs_of(cfg, 3, n=48, seed=5)
     r.score(big, use_graph=True)
     np.testing.assert_array_equal(r.score(small, use_graph=True), eager)
+
+
+# ---------------------------------------------------------------------------
+# candidates of m rows (items spread over m vectors)
+# ---------------------------------------------------------------------------
+
+
+def _mv_check(model, reqs, m, got):
+    per, o = [], 0
+    for p, c in reqs:
+        k = len(c) // m
+        per.append(got[o:o + k])
+        o += k
+    assert o == got.shape[0]
+    for (p, c), s in zip(reqs, per):
+        ref = oracle_mis(model, p, c, m=m)
+        e = score_err(s, ref)
+        assert e <= SCORE_TOL, e
+    return per
+
+
+@pytest.mark.parametrize("m,n_cand", [(2, 8), (3, 50)])
+def test_multivector_tiny(gpu_tiny, m, n_cand):
+    # m = 3 with 50 candidates: 150 branch rows, tiles of 42 whole branches
+    cfg, _, _, model, r = gpu_tiny
+    reqs = [(q.prefix, q.cands) for q in synth.make_requests(1, cfg, m=m, n_cand=n_cand)]
+    for g in (False, True):
+        _mv_check(model, reqs, m, r.score(reqs, use_graph=g, cand_len=m))
+
+
+def test_multivector_qwen(gpu_qwen):
+    cfg, _, _, model, r = gpu_qwen
+    reqs = [(q.prefix, q.cands) for q in synth.make_requests(6, cfg, n_requests=2)]  # m = 8, K = 5 and 20
+    _mv_check(model, reqs, 8, r.score(reqs, cand_len=8))
+
+
+def test_multivector_mis_vs_independent(gpu_qwen):
+    cfg, _, _, _, r = gpu_qwen
+    reqs = [(q.prefix, q.cands) for q in synth.make_requests(2, cfg, m=4, n_cand=12)]
+    mis = r.score(reqs, cand_len=4)
+    ind = r.score(reqs, mode=IND, cand_len=4)
+    e = score_err(mis, ind)
+    print(f"m = 4: GPU MIS vs GPU independent {e:.3e}")
+    assert e <= MIS_VS_IND_TOL
+    # each candidate's branch rows run the same arithmetic in both modes
+    np.testing.assert_array_equal(mis, ind)
+
+
+def test_multivector_batch_and_defaults(gpu_tiny):
+    cfg, _, _, _, r = gpu_tiny
+    a = [(q.prefix, q.cands) for q in synth.make_requests(1, cfg, m=3, n_cand=6)]
+    b = reqs_of(cfg, 4, n=2, n_cand=5)
+    mixed = r.score(a + b, cand_len=[3, 1, 1])
+    np.testing.assert_array_equal(mixed[:6], r.score(a, cand_len=3))
+    np.testing.assert_array_equal(mixed[6:], r.score(b))
+    # cand_len 0 and 1 are the one-row default
+    np.testing.assert_array_equal(r.score(b, cand_len=0), r.score(b))
+    np.testing.assert_array_equal(r.score(b, cand_len=1), r.score(b))
+
+
+def test_multivector_device_entry_and_errors(gpu_tiny):
+    cfg, _, _, _, r = gpu_tiny
+    qs = synth.make_requests(1, cfg, m=2, n_cand=7)
+    ids, L, K = synth.pack_ids(qs)
+    d_ids = torch.from_numpy(ids).cuda()
+    d_s = torch.zeros(int(K.sum()), device="cuda")
+    r.score_dev(L, K, d_ids.data_ptr(), d_s.data_ptr(), cand_len=[2])
+    np.testing.assert_array_equal(d_s.cpu().numpy(), r.score([(q.prefix, q.cands) for q in qs], cand_len=2))
+    p, c = qs[0].prefix, qs[0].cands
+    for bad in (-1, 65):
+        with pytest.raises(spa.DuolmError) as e:
+            r.score([(p, c[:2])], cand_len=[bad]) if bad < 0 else r.score_dev(L, K, d_ids.data_ptr(),
+                                                                            d_s.data_ptr(), cand_len=[bad])
+        assert e.value.status == "EINVAL"
+    with pytest.raises(ValueError):
+        r.score([(p, c[:3])], cand_len=2)
