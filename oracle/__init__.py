@@ -27,3 +27,11 @@ from .ranker import (  # noqa: F401
     widen_bf16,
     widen_f16,
 )
+from .export import (  # noqa: F401
+    export_table,
+    interface_vectors,
+    midpoint_distance,
+    reference_scale,
+    rms,
+    to_fp16_bits,
+)
