@@ -248,6 +248,64 @@ def bench_stress(ranker, cfg, n_req, n_ind):
             "max_abs_diff_mis_vs_independent": float(np.max(np.abs(ref - ind)))}
 
 
+def bench_export(ranker, cfg, reps):
+    """Offline export of the item table: 200,000 encoder outputs of d_model
+    values into FP16 rows (RMS normalise, reference scale, gain), input already
+    in HBM; plus the reference scale over the token embedding.  HBM-bound:
+    algorithmic bytes = rows * d * (input bytes + 2)."""
+    import torch
+    import shared_prefix_scoring_amd as spa
+    import synth
+    n, d = 200_000, cfg.d_model
+    a32 = synth.encoder_outputs(n, d, seed=11)
+    rho = ranker.reference_scale()
+    out = {"rows": n, "d": d, "rho": rho}
+    stream = torch.cuda.current_stream().cuda_stream
+    dz = torch.empty(n * d, dtype=torch.int16, device="cuda")
+    for name, dt, host in (("f32", spa.DUOLM_DTYPE_F32, a32),
+                           ("bf16", spa.DUOLM_DTYPE_BF16, synth.f32_to_bf16_bits(a32))):
+        da = torch.from_numpy(host.view(np.uint8).reshape(-1)).cuda()
+        for _ in range(3):
+            spa.duolm_export_item_vectors(da.data_ptr(), dt, n, d, rho, 0.0, 1e-6, dz.data_ptr(), stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            spa.duolm_export_item_vectors(da.data_ptr(), dt, n, d, rho, 0.0, 1e-6, dz.data_ptr(), stream)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = n * d * (host.itemsize + 2)
+        out[name] = {"us_per_launch": round(us, 1), "rows_per_s": round(n / us * 1e6),
+                     "GBs": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 3)}
+        del da
+    # attainable streaming rate: a plain 16-byte copy of the same byte count as
+    # the fp32 export (819 MB read + 410 MB written ~ 615 MB each way)
+    nb = (n * d * 6 // 2) // 16 * 16
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        spa.duolm_copy_device(dst.data_ptr(), src.data_ptr(), nb, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        spa.duolm_copy_device(dst.data_ptr(), src.data_ptr(), nb, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    out["copy_same_bytes"] = {"us_per_launch": round(us, 1), "GBs": round(2 * nb / us / 1e3, 1)}
+    del src, dst
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ranker.reference_scale()
+    us = (time.perf_counter() - t0) * 1e6 / reps
+    nbytes = cfg.vocab * d * 2
+    out["reference_scale"] = {"us_per_call_incl_sync": round(us, 1), "GBs": round(nbytes / us / 1e3, 1)}
+    return out
+
+
 def summarize_traffic(out_dir, warmup, steps, pool_size):
     """Turn the four counter passes (FETCH_SIZE and WRITE_SIZE of the gate/up
     GEMM in an eager `--no-graph --open-loop 0 --cpu-baseline-s 0` run with the
@@ -347,11 +405,12 @@ def main():
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
     ap.add_argument("--summarize-traffic", metavar="DIR",
                     help="write profiles/traffic_gemm_gateup.json from the counter runs under DIR (no GPU)")
-    ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress"],
+    ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export"],
                     default="headline",
                     help="headline: C=64 x K=100 (the metric); latency: one L=452 x K=100 request per call; "
                          "rating: K=8 at C=8, graph vs eager and ids vs inline vectors; multivec: items of 8 "
-                         "vectors, K in {5,20,50,100}, C=1 and C=8; stress: L=4096 x K=512, MIS vs independent")
+                         "vectors, K in {5,20,50,100}, C=1 and C=8; stress: L=4096 x K=512, MIS vs independent; "
+                         "export: the offline FP16 export of a 200k-row item table")
     args = ap.parse_args()
 
     if args.summarize_traffic:
@@ -382,7 +441,7 @@ def main():
     cfg = synth.QWEN3_0P6B
     log("generating weights and item table")
     w = synth.make_weights(cfg, seed=0)
-    D = synth.make_vid_table(cfg, w)
+    D = synth.make_vid_table(cfg)
     ranker = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
     ranker.load_vid_table(D)
     if args.workload != "headline":
@@ -392,6 +451,8 @@ def main():
             res = bench_latency(ranker, cfg, calls=100)
         elif args.workload == "multivec":
             res = bench_multivec(ranker, cfg, rounds=3)
+        elif args.workload == "export":
+            res = bench_export(ranker, cfg, reps=20)
         else:
             res = bench_stress(ranker, cfg, n_req=16, n_ind=32)
         print(json.dumps({"workload": args.workload, **res}), flush=True)

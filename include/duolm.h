@@ -156,6 +156,57 @@ int duolm_score_batch_dev(duolm_ranker* r, const int32_t* prefix_len, const int3
                           const int32_t* cand_len, int32_t n_req, const int32_t* d_ids, float* d_scores,
                           const duolm_opts* opts);
 
+/*
+ * Offline export of item vectors -- the step that fills the item table
+ * before serving ([digest] 一句话总结 and 核心方法: the continuous-input
+ * interface RMS-normalises the encoder's item representation a, calibrates it
+ * by the reference scale rho of the ranker's native word embeddings and
+ * multiplies a learnable gain e^gamma; 方法步骤详情 step 3: the frozen
+ * vectors are written once as FP16 into the GPU-resident table; onedev.kr
+ * digest, 어떻게 동작하나).  Per row
+ *     z = e^gamma * rho * a / sqrt(mean_k a_k^2 + eps),
+ * evaluated in float64 and rounded once to IEEE binary16 (nearest, ties to
+ * even; magnitudes from 65520 up become +-inf).  A row whose mean square plus
+ * eps is 0 exports as zeros.  eps = 0 is the bare RMS.
+ */
+typedef enum { DUOLM_DTYPE_F32 = 0, DUOLM_DTYPE_BF16 = 1, DUOLM_DTYPE_F16 = 2 } duolm_dtype;
+#define DUOLM_MAX_EXPORT_DIM 8192
+
+/*
+ * Export on the current HIP device, stream-ordered (returns once the work is
+ * enqueued on hip_stream; NULL is the null stream).
+ *   d_a    : device, n_rows x d values of a_dtype, row-major, 16-byte aligned.
+ *   d       : row length, a multiple of 8 in [8, DUOLM_MAX_EXPORT_DIM].
+ *   rho, gamma, eps : finite; eps >= 0.
+ *   d_z    : device, n_rows x d fp16 outputs, 16-byte aligned (caller-owned).
+ * n_rows = 0 is a no-op.  Both buffers must be device memory of the current
+ * device; a pointer that is not, or whose enclosing allocation is shorter than
+ * the stated bytes, is rejected (an overrun inside a larger allocation, as
+ * from a caching allocator's pool, cannot be seen and is the caller's).
+ * Errors: EINVAL (bad dtype, d, n_rows, scale arguments, or a buffer that is
+ * not such device memory), EHIP.
+ */
+int duolm_export_item_vectors(const void* d_a, int32_t a_dtype, int64_t n_rows, int32_t d, double rho,
+                              double gamma, double eps, uint16_t* d_z, void* hip_stream);
+
+/*
+ * Export n_rows encoder outputs (device, [n_rows][d_model] of a_dtype) straight
+ * into the ranker's item table, replacing any previous table: row iota answers
+ * id V + iota, as with duolm_load_vid_table.  Synchronous.
+ * Errors: as duolm_export_item_vectors, plus EINVAL for n_rows < 1 or
+ * V + n_rows over INT32_MAX, ENOMEM.
+ */
+int duolm_export_vid_table(duolm_ranker* r, const void* d_a, int32_t a_dtype, int64_t n_rows, double rho,
+                           double gamma, double eps);
+
+/*
+ * rho: the root mean square over every entry of the ranker's token embedding
+ * matrix (its "native word embeddings"), accumulated in float64 in a fixed
+ * order (the same value on every call).  Synchronous.
+ * Errors: EINVAL (NULL), ENOMEM, EHIP.
+ */
+int duolm_reference_scale(duolm_ranker* r, double* rho);
+
 /* Kernel classes for the profiling counters. */
 typedef enum {
   DUOLM_K_EMBED = 0,      /* VID-aware embedding gather */

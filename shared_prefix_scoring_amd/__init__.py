@@ -6,6 +6,9 @@ the weights-file writer.  Build the library with
 ``python -m shared_prefix_scoring_amd.build``.
 """
 from ._lib import (  # noqa: F401
+    DUOLM_DTYPE_BF16,
+    DUOLM_DTYPE_F16,
+    DUOLM_DTYPE_F32,
     DUOLM_MODE_INDEPENDENT,
     DUOLM_MODE_MIS,
     EPILOGUES,
@@ -17,6 +20,8 @@ from ._lib import (  # noqa: F401
     duolm_copy_device,
     duolm_debug_forward,
     duolm_debug_gemm,
+    duolm_export_item_vectors,
+    duolm_export_vid_table,
     duolm_free_ranker,
     duolm_get_dims,
     duolm_get_kernel_stats,
@@ -24,6 +29,7 @@ from ._lib import (  # noqa: F401
     duolm_load_ranker,
     duolm_load_ranker_mem,
     duolm_load_vid_table,
+    duolm_reference_scale,
     duolm_score_batch,
     duolm_score_batch_dev,
     duolm_set_profiling,

@@ -78,7 +78,14 @@ EXPORTS = {
     "duolm_debug_gemm": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
                                    C.c_int32, C.c_void_p]),
     "duolm_copy_device": (C.c_int, [C.c_void_p, C.c_void_p, C.c_uint64, C.c_void_p]),
+    "duolm_export_item_vectors": (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_double, C.c_double,
+                                            C.c_double, C.c_void_p, C.c_void_p]),
+    "duolm_export_vid_table": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_double, C.c_double,
+                                         C.c_double]),
+    "duolm_reference_scale": (C.c_int, [C.c_void_p, C.POINTER(C.c_double)]),
 }
+
+DUOLM_DTYPE_F32, DUOLM_DTYPE_BF16, DUOLM_DTYPE_F16 = 0, 1, 2
 
 
 def lib() -> C.CDLL:
@@ -231,6 +238,22 @@ def duolm_copy_device(d_dst: int, d_src: int, nbytes: int, stream=None) -> None:
     _check(lib().duolm_copy_device(C.c_void_p(d_dst), C.c_void_p(d_src), nbytes, C.c_void_p(stream or 0)))
 
 
+def duolm_export_item_vectors(d_a: int, a_dtype: int, n_rows: int, d: int, rho: float, gamma: float, eps: float,
+                              d_z: int, stream=None) -> None:
+    _check(lib().duolm_export_item_vectors(C.c_void_p(d_a), a_dtype, n_rows, d, rho, gamma, eps, C.c_void_p(d_z),
+                                           C.c_void_p(stream or 0)))
+
+
+def duolm_export_vid_table(r, d_a: int, a_dtype: int, n_rows: int, rho: float, gamma: float, eps: float) -> None:
+    _check(lib().duolm_export_vid_table(r, C.c_void_p(d_a), a_dtype, n_rows, rho, gamma, eps))
+
+
+def duolm_reference_scale(r) -> float:
+    v = C.c_double()
+    _check(lib().duolm_reference_scale(r, C.byref(v)))
+    return v.value
+
+
 # ----------------------------------------------------------------- convenience
 
 class Ranker:
@@ -251,6 +274,14 @@ class Ranker:
     def load_vid_table(self, rows_fp16: np.ndarray) -> None:
         duolm_load_vid_table(self.h, rows_fp16)
         self.dims = duolm_get_dims(self.h)
+
+    def export_vid_table(self, d_a: int, a_dtype: int, n_rows: int, rho: float, gamma: float = 0.0,
+                         eps: float = 0.0) -> None:
+        duolm_export_vid_table(self.h, d_a, a_dtype, n_rows, rho, gamma, eps)
+        self.dims = duolm_get_dims(self.h)
+
+    def reference_scale(self) -> float:
+        return duolm_reference_scale(self.h)
 
     def score(self, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None,
               cand_len=None) -> np.ndarray:

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libduolm.so")
 
-SOURCES = ["api.cpp", "k_elem.hip", "k_gemm.hip", "k_attn.hip"]
+SOURCES = ["api.cpp", "k_elem.hip", "k_gemm.hip", "k_attn.hip", "k_export.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -986,6 +986,110 @@ int duolm_load_vid_table(duolm_ranker* R, const uint16_t* rows, int64_t n_rows) 
   return DUOLM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// offline export of item vectors (the step before the table is served)
+// ---------------------------------------------------------------------------
+namespace {
+
+// p must be device memory of `device` holding [p, p + bytes) inside one
+// allocation; a host or foreign pointer would fault the kernel instead
+int check_dev_range(const void* p, size_t bytes, int device, const char* what) {
+  if (!p) return fail(DUOLM_EINVAL, "%s is NULL", what);
+  if ((uintptr_t)p % 16) return fail(DUOLM_EINVAL, "%s is not 16-byte aligned", what);
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess || at.type != hipMemoryTypeDevice) {
+    (void)hipGetLastError();
+    return fail(DUOLM_EINVAL, "%s is not device memory", what);
+  }
+  if (at.device != device) return fail(DUOLM_EINVAL, "%s lives on device %d, not %d", what, at.device, device);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DUOLM_EINVAL, "%s: allocation range unknown", what);
+  }
+  if ((const char*)p + bytes > (const char*)base + size)
+    return fail(DUOLM_EINVAL, "%s: %zu bytes do not fit its allocation", what, bytes);
+  return DUOLM_OK;
+}
+
+size_t dtype_bytes(int32_t dt) { return dt == DUOLM_DTYPE_F32 ? 4 : 2; }
+
+int check_export_args(int32_t dt, int64_t n_rows, int32_t d, double rho, double gamma, double eps) {
+  if (dt != DUOLM_DTYPE_F32 && dt != DUOLM_DTYPE_BF16 && dt != DUOLM_DTYPE_F16)
+    return fail(DUOLM_EINVAL, "bad input dtype %d", dt);
+  if (n_rows < 0 || n_rows > INT32_MAX) return fail(DUOLM_EINVAL, "n_rows %lld out of range", (long long)n_rows);
+  if (d < 8 || d % 8 || d > DUOLM_MAX_EXPORT_DIM)
+    return fail(DUOLM_EINVAL, "d = %d: must be a multiple of 8 in [8, %d]", d, DUOLM_MAX_EXPORT_DIM);
+  if (!std::isfinite(rho) || !std::isfinite(gamma) || !(eps >= 0.0) || !std::isfinite(eps))
+    return fail(DUOLM_EINVAL, "rho and gamma must be finite and eps finite and >= 0");
+  if (!std::isfinite(rho * std::exp(gamma))) return fail(DUOLM_EINVAL, "rho * e^gamma overflows");
+  return DUOLM_OK;
+}
+
+}  // namespace
+
+int duolm_export_item_vectors(const void* d_a, int32_t a_dtype, int64_t n_rows, int32_t d, double rho,
+                              double gamma, double eps, uint16_t* d_z, void* hip_stream) {
+  int rc = check_export_args(a_dtype, n_rows, d, rho, gamma, eps);
+  if (rc) return rc;
+  if (n_rows == 0) return DUOLM_OK;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if ((rc = check_dev_range(d_a, (size_t)n_rows * d * dtype_bytes(a_dtype), dev, "d_a"))) return rc;
+  if ((rc = check_dev_range(d_z, (size_t)n_rows * d * 2, dev, "d_z"))) return rc;
+  if (!launch_export((hipStream_t)hip_stream, a_dtype, d_a, n_rows, d, rho * std::exp(gamma), eps, d_z))
+    return fail(DUOLM_EINVAL, "unsupported export shape");
+  HIP_TRY(hipGetLastError());
+  return DUOLM_OK;
+}
+
+int duolm_export_vid_table(duolm_ranker* R, const void* d_a, int32_t a_dtype, int64_t n_rows, double rho,
+                           double gamma, double eps) {
+  if (!R) return fail(DUOLM_EINVAL, "NULL argument");
+  const int d = R->dims.d_model;
+  int rc = check_export_args(a_dtype, n_rows, d, rho, gamma, eps);
+  if (rc) return rc;
+  if (n_rows < 1) return fail(DUOLM_EINVAL, "n_rows must be >= 1");
+  if ((int64_t)R->dims.vocab + n_rows > INT32_MAX) return fail(DUOLM_EINVAL, "V + n_rows exceeds int32 ids");
+  HIP_TRY(hipSetDevice(R->device));
+  if ((rc = check_dev_range(d_a, (size_t)n_rows * d * dtype_bytes(a_dtype), R->device, "d_a"))) return rc;
+  HIP_TRY(hipStreamSynchronize(R->stream));
+  const size_t bytes = (size_t)n_rows * d * 2;
+  uint16_t* p = nullptr;
+  if (hipMalloc((void**)&p, bytes) != hipSuccess) return fail(DUOLM_ENOMEM, "item table (%zu bytes)", bytes);
+  const bool ok = launch_export(R->stream, a_dtype, d_a, n_rows, d, rho * std::exp(gamma), eps, p);
+  const hipError_t e1 = hipGetLastError();
+  const hipError_t e2 = hipStreamSynchronize(R->stream);
+  if (!ok || e1 != hipSuccess || e2 != hipSuccess) {
+    (void)hipFree(p);
+    return fail(DUOLM_EHIP, "item export failed: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  }
+  if (R->vid) (void)hipFree(R->vid);
+  R->vid = p;
+  R->n_vid = n_rows;
+  R->dims.n_vid = n_rows;
+  drop_graphs(R);  // graphs bake the table pointer and size
+  return DUOLM_OK;
+}
+
+int duolm_reference_scale(duolm_ranker* R, double* rho) {
+  if (!R || !rho) return fail(DUOLM_EINVAL, "NULL argument");
+  HIP_TRY(hipSetDevice(R->device));
+  double* buf = nullptr;
+  if (hipMalloc((void**)&buf, (kScaleBlocks + 1) * sizeof(double)) != hipSuccess)
+    return fail(DUOLM_ENOMEM, "reference-scale scratch");
+  launch_reference_scale(R->stream, R->embed, (int64_t)R->dims.vocab * R->dims.d_model, buf, buf + kScaleBlocks);
+  double h = 0.0;
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, buf + kScaleBlocks, sizeof(double), hipMemcpyDeviceToHost, R->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(R->stream);
+  (void)hipFree(buf);
+  if (e != hipSuccess) return fail(DUOLM_EHIP, "reference scale: %s", hipGetErrorString(e));
+  *rho = h;
+  return DUOLM_OK;
+}
+
 int duolm_get_dims(const duolm_ranker* R, duolm_dims* out) {
   if (!R || !out) return fail(DUOLM_EINVAL, "NULL argument");
   *out = R->dims;

@@ -46,4 +46,16 @@ bool attn_supported(int head_dim);
 void launch_attn(hipStream_t s, bool branch, int hd, int cap_items, const uint16_t* QKV, int ld,
                  uint16_t* O, int ldo, DevBatch b, int H, int Hkv, float scale_log2);
 
+// Offline export of encoder outputs a[n_rows, d] (16-byte aligned rows of
+// dtype EXPORT_*) into FP16 rows z = scale * a / sqrt(mean(a^2) + eps).
+// Returns false if d or dtype is unsupported.
+enum { EXPORT_F32 = 0, EXPORT_BF16 = 1, EXPORT_F16 = 2 };
+constexpr int kMaxExportDim = 8192;
+bool launch_export(hipStream_t s, int dtype, const void* a, int64_t n_rows, int d, double scale, double eps,
+                   uint16_t* z);
+// rho = root mean square of n_values bf16 values (n_values % 8 == 0) into
+// rho[0]; partial holds kScaleBlocks doubles of scratch.
+constexpr int kScaleBlocks = 4096;
+void launch_reference_scale(hipStream_t s, const uint16_t* E, int64_t n_values, double* partial, double* rho);
+
 }  // namespace duolm

@@ -139,27 +139,38 @@ def make_weights(cfg: ModelConfig, seed: int = 0, gain_sigma: float = 0.0) -> Di
     return out
 
 
-def make_vid_table(cfg: ModelConfig, weights: Dict[str, np.ndarray] | None = None,
-                   seed: int = 1, n_rows: int | None = None) -> np.ndarray:
+def make_vid_table(cfg: ModelConfig, seed: int = 1, n_rows: int | None = None) -> np.ndarray:
     """Synthetic frozen item vectors z_i, stored fp16 (uint16 bits), shape [N, d].
 
-    Tiny model: rows ~ N(0, 0.02^2).  Larger models: each row is a Gaussian
-    direction with RMS equal to the token-embedding RMS (about 0.02), standing
-    in for the pages' interface output, whose rows are RMS-normalised and
-    rescaled to the ranker's native embedding scale.
+    Rows ~ N(0, 0.02^2) i.i.d., the scale of the token embedding, standing in
+    for the pages' interface output, whose rows are calibrated to the ranker's
+    native embedding scale.  (The export that makes such rows from encoder
+    outputs is a step of its own; its inputs come from encoder_outputs.)
     """
     n = cfg.n_vid if n_rows is None else n_rows
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
     g = rng.standard_normal((n, cfg.d_model), dtype=np.float32)
-    if cfg.name == "tiny":
-        return f32_to_f16_bits(g * np.float32(INIT_STD))
-    if weights is not None:
-        e = bf16_bits_to_f32(weights["embed"][: min(4096, cfg.vocab)])
-        rho = float(np.sqrt(np.mean(e.astype(np.float64) ** 2)))
-    else:
-        rho = INIT_STD
-    row_rms = np.sqrt(np.mean(g.astype(np.float64) ** 2, axis=1, keepdims=True))
-    return f32_to_f16_bits((g / row_rms * rho).astype(np.float32))
+    return f32_to_f16_bits(g * np.float32(INIT_STD))
+
+
+def encoder_outputs(n_rows: int, d: int, seed: int = 11) -> np.ndarray:
+    """Synthetic encoder item representations a_i, float32 [n_rows, d].
+
+    They stand in for the last-layer EOS hidden states of the item encoder
+    (Qwen3-Embedding-0.6B on the pages), whose scale is unrelated to the
+    ranker's embeddings: a_i = r_i * c * g with g ~ N(0, I), a per-row scale
+    r_i = exp(N(0, 0.5^2)) and a per-channel scale c = exp(N(0, 1)) shared by
+    all rows (a few channels far larger than the rest, as hidden states have).
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    chan = np.exp(rng.standard_normal(d)).astype(np.float32)
+    out = np.empty((n_rows, d), dtype=np.float32)
+    step = 65536
+    for i in range(0, n_rows, step):
+        m = min(step, n_rows - i)
+        row = np.exp(0.5 * rng.standard_normal((m, 1))).astype(np.float32)
+        out[i:i + m] = rng.standard_normal((m, d), dtype=np.float32) * chan * row
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -20,7 +20,7 @@ def tiny():
     from oracle import OracleModel
     cfg = synth.TINY
     w = synth.make_weights(cfg, seed=0)
-    D = synth.make_vid_table(cfg, w)
+    D = synth.make_vid_table(cfg)
     return cfg, w, D, OracleModel.from_arrays(cfg, w, D)
 
 
@@ -31,7 +31,7 @@ def tiny_gains():
     from oracle import OracleModel
     cfg = synth.TINY
     w = synth.make_weights(cfg, seed=5, gain_sigma=0.1)
-    D = synth.make_vid_table(cfg, w, seed=6)
+    D = synth.make_vid_table(cfg, seed=6)
     return cfg, w, D, OracleModel.from_arrays(cfg, w, D)
 
 
@@ -41,7 +41,7 @@ def qwen():
     from oracle import OracleModel
     cfg = synth.QWEN3_0P6B
     w = synth.make_weights(cfg, seed=0)
-    D = synth.make_vid_table(cfg, w)
+    D = synth.make_vid_table(cfg)
     return cfg, w, D, OracleModel.from_arrays(cfg, w, D)
 
 

@@ -229,7 +229,7 @@ def test_inline_vectors_without_table(tiny):
     # a ranker with no table loaded scores requests that carry their vectors,
     # and equals a ranker that holds those vectors in its table
     cfg, w, D, _ = tiny
-    D2 = synth.make_vid_table(cfg, w, seed=77)
+    D2 = synth.make_vid_table(cfg, seed=77)
     with_table = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
     no_table = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
     try:
