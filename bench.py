@@ -370,7 +370,7 @@ def summarize_traffic(out_dir, warmup, steps, pool_size):
         "bytes_per_launch": round(meas),
         "algorithmic_bytes_per_launch": round(alg),
         "ratio_measured_to_algorithmic": round(meas / alg, 2),
-        "kernel_src_hash": src_hash("k_gemm.hip", "common.h", "launch.h"),
+        "kernel_src_hash": src_hash("k_gemm.hip", "common.h"),
     }
     path = os.path.join(ROOT, "profiles", "traffic_gemm_gateup.json")
     with open(path, "w") as fh:
@@ -508,7 +508,7 @@ def main():
     br_ms = br.total_ms / max(br.launches, 1)
     br_bytes = br.bytes / max(br.launches, 1)
     achieved = gu_flops / (gu_ms * 1e-3) / 1e12
-    traffic = traffic_from_profile(src_hash("k_gemm.hip", "common.h", "launch.h"))
+    traffic = traffic_from_profile(src_hash("k_gemm.hip", "common.h"))
     out = {
         "metric": METRIC,
         "value": round(value, 1),
