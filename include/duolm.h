@@ -207,6 +207,64 @@ int duolm_export_vid_table(duolm_ranker* r, const void* d_a, int32_t a_dtype, in
  */
 int duolm_reference_scale(duolm_ranker* r, double* rho);
 
+/*
+ * Host input packer.  A request carries only item ids and feedback; the
+ * runtime assembles the ranker input from them ([digest] 方法步骤详情 step 4).
+ * The input reads: the instruction, then for every history item a marker
+ * token, the item's vector(s) and its feedback text, then the candidate
+ * header, then the candidates' vectors ([onedev] 어떻게 동작하나; packing after
+ * the shared prefix: 어떻게 쓰나).  The pages found this CPU-side input
+ * compilation to be the bottleneck of their runtime near 200 requests/s
+ * ([digest] 实验结果); here it is plain id copying in C++, optionally spread
+ * over threads.  Feedback text arrives as token ids: nothing is tokenised.
+ * Host only: no GPU work, and ids are not range-checked (scoring checks them).
+ */
+typedef struct {
+  const int32_t* instruction; /* n_instruction ids opening every request */
+  int32_t n_instruction;
+  int32_t marker;             /* id opening every history item */
+  const int32_t* cand_header; /* n_cand_header ids after the history, before the candidates */
+  int32_t n_cand_header;
+} duolm_template;
+
+typedef struct {
+  int32_t n_items;             /* history items, oldest first (>= 0) */
+  int32_t item_len;            /* VIDs per history item: 0 or 1 means one, up to DUOLM_MAX_CAND_LEN */
+  const int32_t* item_vids;    /* n_items * max(item_len, 1) VIDs, item-major */
+  const int32_t* feedback;     /* the items' feedback ids, concatenated */
+  const int32_t* feedback_off; /* n_items + 1 non-decreasing offsets into feedback, starting at 0 */
+  const int32_t* cand_vids;    /* n_cand * max(cand_len, 1) VIDs, candidate-major */
+  int32_t n_cand;              /* >= 1 */
+  int32_t cand_len;            /* VIDs per candidate, as in duolm_request */
+} duolm_history;
+
+/* Number of ids duolm_pack_requests writes for these requests.
+ * Errors: EINVAL (NULL, n_req < 1, a malformed request or template). */
+int duolm_packed_size(const duolm_template* t, const duolm_history* reqs, int32_t n_req, int64_t* n_ids);
+
+/*
+ * Assemble n_req requests into ids (host, ids_cap int32) as
+ * [prefix_0, cands_0, prefix_1, cands_1, ...], and write each request's
+ * prefix length, candidate count and ids per candidate (host arrays of
+ * n_req): the inputs of duolm_score_packed, or of duolm_score_batch_dev once
+ * ids are on the device.  n_threads 0 or 1 packs on the calling thread; more
+ * (up to 64) splits the requests into contiguous ranges of about equal id
+ * counts, packed in parallel; the output is the same.
+ * Errors: EINVAL (as duolm_packed_size, or ids_cap too small, or NULL outputs).
+ */
+int duolm_pack_requests(const duolm_template* t, const duolm_history* reqs, int32_t n_req, int32_t n_threads,
+                        int32_t* ids, int64_t ids_cap, int32_t* prefix_len, int32_t* n_cand, int32_t* cand_len);
+
+/*
+ * Score a packed batch held in host memory (as duolm_pack_requests writes it):
+ * ids are range-checked while being copied into the handle's page-locked
+ * staging buffer and go up by DMA from there; scores come back the same way
+ * into `scores` (host, sum(n_cand) floats).  cand_len may be NULL.
+ * Synchronous.  Errors: as duolm_score_batch.
+ */
+int duolm_score_packed(duolm_ranker* r, const int32_t* prefix_len, const int32_t* n_cand, const int32_t* cand_len,
+                       int32_t n_req, const int32_t* ids, float* scores, const duolm_opts* opts);
+
 /* Kernel classes for the profiling counters. */
 typedef enum {
   DUOLM_K_EMBED = 0,      /* VID-aware embedding gather */

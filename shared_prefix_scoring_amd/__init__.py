@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     STAGES,
     DuolmError,
+    PackInput,
     Ranker,
     duolm_copy_device,
     duolm_debug_forward,
@@ -29,9 +30,12 @@ from ._lib import (  # noqa: F401
     duolm_load_ranker,
     duolm_load_ranker_mem,
     duolm_load_vid_table,
+    duolm_pack_requests,
+    duolm_packed_size,
     duolm_reference_scale,
     duolm_score_batch,
     duolm_score_batch_dev,
+    duolm_score_packed,
     duolm_set_profiling,
     lib,
 )

@@ -54,6 +54,17 @@ class duolm_opts(C.Structure):
     _fields_ = [("mode", C.c_int32), ("use_graph", C.c_int32), ("hip_stream", C.c_void_p)]
 
 
+class duolm_template(C.Structure):
+    _fields_ = [("instruction", C.c_void_p), ("n_instruction", C.c_int32), ("marker", C.c_int32),
+                ("cand_header", C.c_void_p), ("n_cand_header", C.c_int32)]
+
+
+class duolm_history(C.Structure):
+    _fields_ = [("n_items", C.c_int32), ("item_len", C.c_int32), ("item_vids", C.c_void_p),
+                ("feedback", C.c_void_p), ("feedback_off", C.c_void_p), ("cand_vids", C.c_void_p),
+                ("n_cand", C.c_int32), ("cand_len", C.c_int32)]
+
+
 class duolm_kernel_stats(C.Structure):
     _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("flops", C.c_double), ("bytes", C.c_double)]
 
@@ -83,6 +94,12 @@ EXPORTS = {
     "duolm_export_vid_table": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_double, C.c_double,
                                          C.c_double]),
     "duolm_reference_scale": (C.c_int, [C.c_void_p, C.POINTER(C.c_double)]),
+    "duolm_packed_size": (C.c_int, [C.POINTER(duolm_template), C.POINTER(duolm_history), C.c_int32,
+                                    C.POINTER(C.c_int64)]),
+    "duolm_pack_requests": (C.c_int, [C.POINTER(duolm_template), C.POINTER(duolm_history), C.c_int32, C.c_int32,
+                                      C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "duolm_score_packed": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                     C.c_void_p, C.POINTER(duolm_opts)]),
 }
 
 DUOLM_DTYPE_F32, DUOLM_DTYPE_BF16, DUOLM_DTYPE_F16 = 0, 1, 2
@@ -254,6 +271,66 @@ def duolm_reference_scale(r) -> float:
     return v.value
 
 
+class PackInput:
+    """Structured requests marshalled for the packer: keeps the arrays alive.
+
+    instruction, cand_header: id sequences shared by the batch; marker: id.
+    histories: per request (item_vids [n_items, m_item] or [n_items*m_item],
+    feedbacks: list of id arrays, one per item, cand_vids [K*m_cand],
+    item_len, cand_len)."""
+
+    def __init__(self, instruction, marker: int, histories, cand_header=()):
+        self._keep = []
+        ins = self._arr(instruction)
+        hdr = self._arr(cand_header)
+        self.tpl = duolm_template(ins.ctypes.data if ins.size else None, ins.size, int(marker),
+                                  hdr.ctypes.data if hdr.size else None, hdr.size)
+        self.reqs = (duolm_history * len(histories))()
+        for i, (vids, fbs, cands, item_len, cand_len) in enumerate(histories):
+            v = self._arr(vids)
+            fb = self._arr(np.concatenate([np.asarray(f, np.int32) for f in fbs]) if len(fbs) else [])
+            fo = self._arr(np.concatenate([[0], np.cumsum([len(f) for f in fbs])]) if len(fbs) else [0])
+            c = self._arr(cands)
+            self.reqs[i] = duolm_history(len(fbs), int(item_len), v.ctypes.data if v.size else None,
+                                         fb.ctypes.data if fb.size else None, fo.ctypes.data, c.ctypes.data,
+                                         c.size // max(int(cand_len), 1), int(cand_len))
+        self.n = len(histories)
+
+    def _arr(self, a):
+        a = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+        self._keep.append(a)
+        return a
+
+
+def duolm_packed_size(p: PackInput) -> int:
+    n = C.c_int64()
+    _check(lib().duolm_packed_size(C.byref(p.tpl), p.reqs, p.n, C.byref(n)))
+    return n.value
+
+
+def duolm_pack_requests(p: PackInput, n_threads: int = 1, ids: np.ndarray | None = None):
+    """Returns (ids, prefix_len, n_cand, cand_len) as int32 arrays; `ids` may be
+    a caller buffer (for instance page-locked) of at least the packed size."""
+    if ids is None:
+        ids = np.empty(duolm_packed_size(p), dtype=np.int32)
+    L, K, M = (np.empty(p.n, dtype=np.int32) for _ in range(3))
+    _check(lib().duolm_pack_requests(C.byref(p.tpl), p.reqs, p.n, n_threads, ids.ctypes.data, ids.size,
+                                     L.ctypes.data, K.ctypes.data, M.ctypes.data))
+    return ids, L, K, M
+
+
+def duolm_score_packed(r, prefix_len, n_cand, cand_len, ids, mode: int = DUOLM_MODE_MIS, use_graph: bool = True,
+                       stream=None) -> np.ndarray:
+    L, K = _i32(prefix_len), _i32(n_cand)
+    M = None if cand_len is None else _i32(cand_len)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    out = np.empty(int(K.sum()), dtype=np.float32)
+    o = _opts(mode, use_graph, stream)
+    _check(lib().duolm_score_packed(r, L.ctypes.data, K.ctypes.data, None if M is None else M.ctypes.data,
+                                    L.shape[0], ids.ctypes.data, out.ctypes.data, C.byref(o)))
+    return out
+
+
 # ----------------------------------------------------------------- convenience
 
 class Ranker:
@@ -286,6 +363,10 @@ class Ranker:
     def score(self, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None,
               cand_len=None) -> np.ndarray:
         return duolm_score_batch(self.h, reqs, mode, use_graph, stream, cand_len)
+
+    def score_packed(self, prefix_len, n_cand, cand_len, ids, mode: int = DUOLM_MODE_MIS,
+                     use_graph: bool = True, stream=None) -> np.ndarray:
+        return duolm_score_packed(self.h, prefix_len, n_cand, cand_len, ids, mode, use_graph, stream)
 
     def score_dev(self, prefix_len, n_cand, d_ids: int, d_scores: int, mode: int = DUOLM_MODE_MIS,
                   use_graph: bool = True, stream=None, cand_len=None) -> None:

@@ -28,6 +28,7 @@
 #include <cstring>
 #include <map>
 #include <string>
+#include <thread>
 #include <tuple>
 #include <vector>
 
@@ -154,6 +155,8 @@ struct duolm_ranker {
   int32_t call_n_inline = 0;
   int32_t* d_err = nullptr;
   int32_t* h_err = nullptr;  // pinned
+  char* h_stage = nullptr;   // pinned staging for host ids in and host scores out
+  size_t cap_stage = 0;
   // descriptor block
   int cap_seq = 0, cap_pi = 0, cap_bi = 0, cap_hs = 0;
   size_t off_sro = 0, off_seq = 0, off_pi = 0, off_bi = 0, off_hr = 0, meta_bytes = 0;
@@ -738,6 +741,20 @@ int max_cand_len(const duolm_ranker* R) {
   return std::min(DUOLM_MAX_CAND_LEN, attn_rows_per_item(true, R->dims.n_heads / R->dims.n_kv_heads));
 }
 
+// Pinned host staging, so that host ids go up and scores come down by DMA
+// straight from page-locked memory.  Calls are synchronous, so nothing is in
+// flight from it when it grows.
+int ensure_stage(duolm_ranker* R, size_t bytes) {
+  if (bytes <= R->cap_stage) return DUOLM_OK;
+  const size_t cap = std::max(bytes, R->cap_stage * 2);
+  char* p = nullptr;
+  if (hipHostMalloc((void**)&p, cap) != hipSuccess) return fail(DUOLM_ENOMEM, "pinned staging (%zu bytes)", cap);
+  if (R->h_stage) (void)hipHostFree(R->h_stage);
+  R->h_stage = p;
+  R->cap_stage = cap;
+  return DUOLM_OK;
+}
+
 int validate_lengths(duolm_ranker* R, const CallInput& in, int64_t& total_ids, int64_t& total_scores) {
   if (in.n_req < 1) return fail(DUOLM_EINVAL, "n_req must be >= 1");
   total_ids = 0;
@@ -816,8 +833,12 @@ int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool id
   rc = validate_lengths(R, in, total_ids, total_scores);
   if (rc) return rc;
   HIP_TRY(hipSetDevice(R->device));
+  const bool stage = !ids_dev || !out_dev;
+  if (stage && (rc = ensure_stage(R, (size_t)std::max(total_ids, total_scores) * 4))) return rc;
   if (!ids_dev) {
+    // range-check the host ids while copying them into the pinned stage
     const int64_t lim = (int64_t)R->dims.vocab + R->n_vid + n_inline;
+    int32_t* st = (int32_t*)R->h_stage;
     for (int64_t i = 0; i < total_ids; ++i) {
       const int32_t id = ids[i];
       if (id < 0 || id >= lim) {
@@ -825,7 +846,9 @@ int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool id
           return fail(DUOLM_ESTATE, "id %d at position %lld is a VID but no item table is loaded", id, (long long)i);
         return fail(DUOLM_ERANGE, "id %d at position %lld outside [0, %lld)", id, (long long)i, (long long)lim);
       }
+      st[i] = id;
     }
+    ids = st;
   }
   std::vector<Plan> plans;
   build_plans(R, in, mode, plans);
@@ -872,9 +895,10 @@ int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool id
     }
   }
   if (*R->h_err) return fail(DUOLM_ERANGE, "an id in the device batch is outside [0, V + N)");
-  HIP_TRY(hipMemcpyAsync(out, R->d_out, (size_t)total_scores * 4,
+  HIP_TRY(hipMemcpyAsync(out_dev ? (void*)out : (void*)R->h_stage, R->d_out, (size_t)total_scores * 4,
                          out_dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
+  if (!out_dev) memcpy(out, R->h_stage, (size_t)total_scores * 4);
   return DUOLM_OK;
 }
 
@@ -1090,6 +1114,129 @@ int duolm_reference_scale(duolm_ranker* R, double* rho) {
   return DUOLM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// host input packer
+// ---------------------------------------------------------------------------
+namespace {
+
+int64_t history_prefix_len(const duolm_template& t, const duolm_history& h) {
+  const int64_t per_item_vids = h.item_len > 1 ? h.item_len : 1;
+  return (int64_t)t.n_instruction + (int64_t)h.n_items * (1 + per_item_vids) +
+         (h.n_items > 0 ? (int64_t)h.feedback_off[h.n_items] : 0) + t.n_cand_header;
+}
+
+int check_history(const duolm_template& t, const duolm_history& h, int i) {
+  if (h.n_items < 0) return fail(DUOLM_EINVAL, "request %d: n_items < 0", i);
+  if (h.item_len < 0 || h.item_len > DUOLM_MAX_CAND_LEN)
+    return fail(DUOLM_EINVAL, "request %d: item_len %d outside [0, %d]", i, h.item_len, DUOLM_MAX_CAND_LEN);
+  if (h.cand_len < 0 || h.cand_len > DUOLM_MAX_CAND_LEN)
+    return fail(DUOLM_EINVAL, "request %d: cand_len %d outside [0, %d]", i, h.cand_len, DUOLM_MAX_CAND_LEN);
+  if (h.n_cand < 1) return fail(DUOLM_EINVAL, "request %d: n_cand must be >= 1", i);
+  if (!h.cand_vids) return fail(DUOLM_EINVAL, "request %d: NULL cand_vids", i);
+  if (h.n_items > 0) {
+    if (!h.item_vids || !h.feedback_off) return fail(DUOLM_EINVAL, "request %d: NULL item arrays", i);
+    if (h.feedback_off[0] != 0) return fail(DUOLM_EINVAL, "request %d: feedback_off[0] != 0", i);
+    for (int j = 0; j < h.n_items; ++j)
+      if (h.feedback_off[j + 1] < h.feedback_off[j])
+        return fail(DUOLM_EINVAL, "request %d: feedback_off decreases at item %d", i, j);
+    if (h.feedback_off[h.n_items] > 0 && !h.feedback) return fail(DUOLM_EINVAL, "request %d: NULL feedback", i);
+  }
+  const int64_t L = history_prefix_len(t, h);
+  if (L < 1) return fail(DUOLM_EINVAL, "request %d: empty prefix", i);
+  if (L > INT32_MAX / 2) return fail(DUOLM_EINVAL, "request %d: prefix too long", i);
+  return DUOLM_OK;
+}
+
+// instruction, (marker, item VIDs, feedback) per item, header, candidates
+void assemble_one(const duolm_template& t, const duolm_history& h, int32_t* o) {
+  const int m_item = h.item_len > 1 ? h.item_len : 1, m_cand = h.cand_len > 1 ? h.cand_len : 1;
+  if (t.n_instruction) memcpy(o, t.instruction, (size_t)t.n_instruction * 4);
+  o += t.n_instruction;
+  for (int j = 0; j < h.n_items; ++j) {
+    *o++ = t.marker;
+    memcpy(o, h.item_vids + (size_t)j * m_item, (size_t)m_item * 4);
+    o += m_item;
+    const int32_t f0 = h.feedback_off[j], f1 = h.feedback_off[j + 1];
+    if (f1 > f0) memcpy(o, h.feedback + f0, (size_t)(f1 - f0) * 4);
+    o += f1 - f0;
+  }
+  if (t.n_cand_header) memcpy(o, t.cand_header, (size_t)t.n_cand_header * 4);
+  o += t.n_cand_header;
+  memcpy(o, h.cand_vids, (size_t)h.n_cand * m_cand * 4);
+}
+
+int check_template(const duolm_template* t) {
+  if (!t) return fail(DUOLM_EINVAL, "NULL template");
+  if (t->n_instruction < 0 || t->n_cand_header < 0) return fail(DUOLM_EINVAL, "negative template length");
+  if ((t->n_instruction && !t->instruction) || (t->n_cand_header && !t->cand_header))
+    return fail(DUOLM_EINVAL, "NULL template array");
+  return DUOLM_OK;
+}
+
+}  // namespace
+
+int duolm_packed_size(const duolm_template* t, const duolm_history* reqs, int32_t n_req, int64_t* n_ids) {
+  if (!reqs || !n_ids || n_req < 1) return fail(DUOLM_EINVAL, "NULL argument or n_req < 1");
+  int rc = check_template(t);
+  if (rc) return rc;
+  int64_t total = 0;
+  for (int i = 0; i < n_req; ++i) {
+    if ((rc = check_history(*t, reqs[i], i))) return rc;
+    total += history_prefix_len(*t, reqs[i]) + (int64_t)reqs[i].n_cand * std::max(reqs[i].cand_len, 1);
+  }
+  *n_ids = total;
+  return DUOLM_OK;
+}
+
+int duolm_pack_requests(const duolm_template* t, const duolm_history* reqs, int32_t n_req, int32_t n_threads,
+                        int32_t* ids, int64_t ids_cap, int32_t* prefix_len, int32_t* n_cand, int32_t* cand_len) {
+  if (!ids || !prefix_len || !n_cand || !cand_len) return fail(DUOLM_EINVAL, "NULL output");
+  if (n_threads < 0) return fail(DUOLM_EINVAL, "n_threads < 0");
+  int64_t total = 0;
+  int rc = duolm_packed_size(t, reqs, n_req, &total);
+  if (rc) return rc;
+  if (total > ids_cap) return fail(DUOLM_EINVAL, "ids_cap %lld < %lld ids needed", (long long)ids_cap, (long long)total);
+  // offsets first (one cheap pass), then the copies, split into contiguous
+  // request ranges across threads; every range writes only its own slots
+  std::vector<int64_t> off((size_t)n_req + 1, 0);
+  for (int i = 0; i < n_req; ++i)
+    off[i + 1] = off[i] + history_prefix_len(*t, reqs[i]) + (int64_t)reqs[i].n_cand * std::max(reqs[i].cand_len, 1);
+  auto work = [&](int lo, int hi) {
+    for (int i = lo; i < hi; ++i) {
+      assemble_one(*t, reqs[i], ids + off[i]);
+      prefix_len[i] = (int32_t)history_prefix_len(*t, reqs[i]);
+      n_cand[i] = reqs[i].n_cand;
+      cand_len[i] = std::max(reqs[i].cand_len, 1);
+    }
+  };
+  const int nt = std::min({std::max(n_threads, 1), (int)n_req, 64});
+  if (nt == 1) {
+    work(0, n_req);
+    return DUOLM_OK;
+  }
+  // balance by ids, not by request count
+  std::vector<int> cut((size_t)nt + 1, n_req);
+  cut[0] = 0;
+  for (int k = 1, i = 0; k < nt; ++k) {
+    const int64_t goal = total * k / nt;
+    while (i < n_req && off[i] < goal) ++i;
+    cut[k] = std::max(i, cut[k - 1]);
+  }
+  std::vector<std::thread> th;
+  th.reserve(nt - 1);
+  for (int k = 1; k < nt; ++k) th.emplace_back(work, cut[k], cut[k + 1]);
+  work(cut[0], cut[1]);
+  for (auto& x : th) x.join();
+  return DUOLM_OK;
+}
+
+int duolm_score_packed(duolm_ranker* R, const int32_t* prefix_len, const int32_t* n_cand, const int32_t* cand_len,
+                       int32_t n_req, const int32_t* ids, float* scores, const duolm_opts* opts) {
+  if (!R || !prefix_len || !n_cand || !ids || !scores) return fail(DUOLM_EINVAL, "NULL argument");
+  CallInput in{prefix_len, n_cand, cand_len, n_req};
+  return score_impl(R, in, ids, false, scores, false, opts);
+}
+
 int duolm_get_dims(const duolm_ranker* R, duolm_dims* out) {
   if (!R || !out) return fail(DUOLM_EINVAL, "NULL argument");
   *out = R->dims;
@@ -1148,6 +1295,7 @@ void duolm_free_ranker(duolm_ranker* R) {
   if (R->d_inline) (void)hipFree(R->d_inline);
   if (R->d_err) (void)hipFree(R->d_err);
   if (R->h_err) (void)hipHostFree(R->h_err);
+  if (R->h_stage) (void)hipHostFree(R->h_stage);
   if (R->d_meta) (void)hipFree(R->d_meta);
   for (char* h : R->h_meta)
     if (h) (void)hipHostFree(h);

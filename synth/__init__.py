@@ -183,6 +183,10 @@ class Request:
     prefix: np.ndarray      # int32 [L]: instruction, then (marker, VID x m, feedback...) per item
     cands: np.ndarray       # int32 [K*m]: candidate VIDs (V + row), m per candidate, candidate-major
     m: int = 1              # item vectors per item (history and candidates)
+    # the same request in the structured form a client sends (ids only, no
+    # prefix): history VIDs [n_items, m] and each item's feedback ids
+    items: np.ndarray = None
+    feedback: List[np.ndarray] = None
 
     @property
     def L(self) -> int:
@@ -229,6 +233,11 @@ def _template(cfg: ModelConfig, seed: int, n_instr: int):
     return marker, instr
 
 
+def template(config_id: int, cfg: ModelConfig, seed: int | None = None):
+    """(marker id, instruction ids) shared by every request of workload config_id."""
+    return _template(cfg, config_id if seed is None else seed, WORKLOADS[config_id].n_instr)
+
+
 def make_requests(config_id: int, cfg: ModelConfig, n_requests: int | None = None,
                   seed: int | None = None, n_cand: int | None = None, m: int | None = None) -> List[Request]:
     """Synthetic requests for workload `config_id` (1..6).
@@ -264,6 +273,7 @@ def make_requests(config_id: int, cfg: ModelConfig, n_requests: int | None = Non
         rows = _distinct(rng, N, (n + k) * m)
         hist, cand = rows[:n * m], rows[n * m:]
         parts = [instr]
+        fbs = []
         for i in range(n):
             if isinstance(wl.feedback, tuple):
                 _, mean, lo, hi = wl.feedback
@@ -271,10 +281,12 @@ def make_requests(config_id: int, cfg: ModelConfig, n_requests: int | None = Non
             else:
                 f = int(wl.feedback)
             fb = rng.integers(0, V, size=f).astype(np.int32)
+            fbs.append(fb)
             parts.append(np.concatenate([[marker], V + hist[i * m:(i + 1) * m]]).astype(np.int32))
             parts.append(fb)
         prefix = np.concatenate(parts).astype(np.int32)
-        reqs.append(Request(prefix=prefix, cands=(V + cand).astype(np.int32), m=m))
+        reqs.append(Request(prefix=prefix, cands=(V + cand).astype(np.int32), m=m,
+                            items=(V + hist).astype(np.int32).reshape(n, m), feedback=fbs))
     return reqs
 
 
