@@ -65,14 +65,19 @@ def cpu_baseline(cfg, w, D, reqs, budget_s):
                       f"float64 NumPy, {dt:.1f} s"}
 
 
-def open_loop(ranker, pool, rate, n_requests, seed, C, use_graph, stream):
+def open_loop(ranker, pack, rate, n_requests, seed, C, use_graph, stream):
     """Poisson arrivals at `rate` requests/s; the server takes up to C queued
-    requests per call through the host-buffer entry point (ids copied to the
-    device, scores copied back: the PCIe-inclusive serving path).  Returns
-    per-request latencies (completion - arrival) in ms and the wall time."""
+    requests per call.  Each call runs the whole serving path from structured
+    requests (item VIDs, feedback ids, candidate VIDs): the host packer
+    assembles the ranker input, ids go up from the page-locked staging buffer,
+    scores come back the same way (PCIe-inclusive).  `pack` holds the pool's
+    requests, marshalled once.  Returns per-request latencies (completion -
+    arrival) in ms and the wall time."""
     import synth
+    import shared_prefix_scoring_amd as spa
     arrivals = synth.poisson_arrivals(n_requests, rate, seed)
     lat = np.empty(n_requests)
+    buf = np.empty(spa.duolm_packed_size(pack), dtype=np.int32)
     t0 = time.perf_counter()
     nxt = 0
     while nxt < n_requests:
@@ -83,12 +88,74 @@ def open_loop(ranker, pool, rate, n_requests, seed, C, use_graph, stream):
         end = nxt
         while end < n_requests and end - nxt < C and arrivals[end] <= now:
             end += 1
-        batch = [pool[i % len(pool)] for i in range(nxt, end)]
-        ranker.score([(r.prefix, r.cands) for r in batch], use_graph=use_graph, stream=stream)
+        start = nxt % pack.n
+        cnt = min(end - nxt, pack.n - start)
+        ids, L, K, M = spa.duolm_pack_requests(pack, ids=buf, start=start, count=cnt)
+        ranker.score_packed(L, K, M, ids, use_graph=use_graph, stream=stream)
         done = time.perf_counter() - t0
-        lat[nxt:end] = (done - arrivals[nxt:end]) * 1e3
-        nxt = end
+        lat[nxt:nxt + cnt] = (done - arrivals[nxt:nxt + cnt]) * 1e3
+        nxt += cnt
     return lat, time.perf_counter() - t0
+
+
+def pack_pool(pool, cid, cfg):
+    import shared_prefix_scoring_amd as spa
+    import synth
+    marker, instr = synth.template(cid, cfg)
+    return spa.PackInput(instr, marker, [(r.items, r.feedback, r.cands, r.m, r.m) for r in pool])
+
+
+def bench_packer(ranker, cfg):
+    """The host input packer ([digest] 实验结果: the pages' single-process CPU
+    input compilation failed 1,491 times at 200 requests/s).  Packing rate of
+    the headline pool (10,000 requests, C = 64 per call) on 1 and 8 threads;
+    the host serving path (pack + score from page-locked staging) against the
+    device entry point; and a 200 requests/s Poisson open loop."""
+    import torch
+    import shared_prefix_scoring_amd as spa
+    import synth
+    pool = synth.make_requests(3, cfg)
+    pack = pack_pool(pool, 3, cfg)
+    buf = np.empty(spa.duolm_packed_size(pack), dtype=np.int32)
+    out = {}
+    for nt in (1, 8):
+        t0 = time.perf_counter()
+        for s in range(0, pack.n, 64):
+            spa.duolm_pack_requests(pack, n_threads=nt, ids=buf, start=s, count=min(64, pack.n - s))
+        dt = time.perf_counter() - t0
+        out[f"pack_requests_per_s_{nt}thr"] = round(pack.n / dt)
+    t0 = time.perf_counter()
+    spa.duolm_pack_requests(pack, n_threads=8, ids=buf)
+    dt = time.perf_counter() - t0
+    out["pack_10k_one_call_8thr_ms"] = round(dt * 1e3, 2)
+    stream = torch.cuda.current_stream().cuda_stream
+    calls = 20
+    for s in range(0, 64 * 3, 64):  # warm the shape buckets
+        ids, L, K, M = spa.duolm_pack_requests(pack, ids=buf, start=s, count=64)
+        ranker.score_packed(L, K, M, ids, stream=stream)
+    t0 = time.perf_counter()
+    for c in range(calls):
+        ids, L, K, M = spa.duolm_pack_requests(pack, ids=buf, start=64 * c, count=64)
+        ranker.score_packed(L, K, M, ids, stream=stream)
+    host_ms = (time.perf_counter() - t0) * 1e3 / calls
+    dev = []
+    for c in range(calls):
+        ids, L, K, M = spa.duolm_pack_requests(pack, ids=buf, start=64 * c, count=64)
+        dev.append((torch.from_numpy(ids.copy()).cuda(), L, K, M,
+                    torch.empty(int(K.sum()), dtype=torch.float32, device="cuda")))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for d_ids, L, K, M, d_out in dev:
+        ranker.score_dev(L, K, d_ids.data_ptr(), d_out.data_ptr(), stream=stream, cand_len=M)
+    torch.cuda.synchronize()
+    dev_ms = (time.perf_counter() - t0) * 1e3 / calls
+    out["host_path_call_ms"] = round(host_ms, 3)
+    out["device_path_call_ms"] = round(dev_ms, 3)
+    lat, wall = open_loop(ranker, pack, 200.0, 2000, 300, 64, True, stream)
+    out["open_loop_200rps"] = {"requests": 2000, "p50_ms": round(float(np.percentile(lat, 50)), 2),
+                               "p99_ms": round(float(np.percentile(lat, 99)), 2),
+                               "achieved_rps": round(2000 / wall, 1)}
+    return out
 
 
 def bench_rating(ranker, cfg, D, C, rounds):
@@ -405,12 +472,13 @@ def main():
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
     ap.add_argument("--summarize-traffic", metavar="DIR",
                     help="write profiles/traffic_gemm_gateup.json from the counter runs under DIR (no GPU)")
-    ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export"],
+    ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export", "packer"],
                     default="headline",
                     help="headline: C=64 x K=100 (the metric); latency: one L=452 x K=100 request per call; "
                          "rating: K=8 at C=8, graph vs eager and ids vs inline vectors; multivec: items of 8 "
                          "vectors, K in {5,20,50,100}, C=1 and C=8; stress: L=4096 x K=512, MIS vs independent; "
-                         "export: the offline FP16 export of a 200k-row item table")
+                         "export: the offline FP16 export of a 200k-row item table; packer: the host input "
+                         "packer and the host serving path")
     args = ap.parse_args()
 
     if args.summarize_traffic:
@@ -453,6 +521,8 @@ def main():
             res = bench_multivec(ranker, cfg, rounds=3)
         elif args.workload == "export":
             res = bench_export(ranker, cfg, reps=20)
+        elif args.workload == "packer":
+            res = bench_packer(ranker, cfg)
         else:
             res = bench_stress(ranker, cfg, n_req=16, n_ind=32)
         print(json.dumps({"workload": args.workload, **res}), flush=True)
@@ -542,10 +612,12 @@ def main():
     if args.open_loop > 0:
         log("open-loop Poisson run")
         req_rate = value / 100.0 * 0.9
+        pack = pack_pool(pool, 3, cfg)
         # prime the graphs of the batch sizes the open loop will produce
         for c in range(1, C + 1):
-            ranker.score([(r.prefix, r.cands) for r in pool[:c]], use_graph=use_graph, stream=stream)
-        ol_lat, ol_wall = open_loop(ranker, pool, req_rate, args.open_loop, seed=103, C=C,
+            ids, L, K, M = spa.duolm_pack_requests(pack, count=c)
+            ranker.score_packed(L, K, M, ids, use_graph=use_graph, stream=stream)
+        ol_lat, ol_wall = open_loop(ranker, pack, req_rate, args.open_loop, seed=103, C=C,
                                     use_graph=use_graph, stream=stream)
         out["p99_ms"] = round(float(np.percentile(ol_lat, 99)), 3)
         out["open_loop"] = {"arrivals": "Poisson", "rate_req_per_s": round(req_rate, 1),
@@ -553,7 +625,8 @@ def main():
                             "p50_ms": round(float(np.percentile(ol_lat, 50)), 3),
                             "p99_ms": out["p99_ms"],
                             "scores_per_s": round(args.open_loop * 100 / ol_wall, 1),
-                            "path": "host ids and host scores (PCIe-inclusive)"}
+                            "path": "structured requests -> host packer -> page-locked staging -> "
+                                    "scores to host (PCIe-inclusive)"}
     if args.breakdown:
         ranker.set_profiling(spa.KERNEL_CLASSES)
         for i in range(min(5, len(batches))):

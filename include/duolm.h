@@ -248,8 +248,10 @@ int duolm_packed_size(const duolm_template* t, const duolm_history* reqs, int32_
  * prefix length, candidate count and ids per candidate (host arrays of
  * n_req): the inputs of duolm_score_packed, or of duolm_score_batch_dev once
  * ids are on the device.  n_threads 0 or 1 packs on the calling thread; more
- * (up to 64) splits the requests into contiguous ranges of about equal id
- * counts, packed in parallel; the output is the same.
+ * (up to 64, and at most one per 65,536 ids of work, since starting a thread
+ * costs about as much as copying that many ids) splits the requests into
+ * contiguous ranges of about equal id counts, packed in parallel; the output
+ * is the same.
  * Errors: EINVAL (as duolm_packed_size, or ids_cap too small, or NULL outputs).
  */
 int duolm_pack_requests(const duolm_template* t, const duolm_history* reqs, int32_t n_req, int32_t n_threads,

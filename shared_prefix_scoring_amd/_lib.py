@@ -302,21 +302,33 @@ class PackInput:
         return a
 
 
-def duolm_packed_size(p: PackInput) -> int:
+def _slice(p: PackInput, start: int, count):
+    count = p.n - start if count is None else count
+    if start < 0 or count < 1 or start + count > p.n:
+        raise ValueError("request range out of bounds")
+    ptr = C.cast(C.addressof(p.reqs) + start * C.sizeof(duolm_history), C.POINTER(duolm_history))
+    return ptr, count
+
+
+def duolm_packed_size(p: PackInput, start: int = 0, count: int | None = None) -> int:
+    ptr, count = _slice(p, start, count)
     n = C.c_int64()
-    _check(lib().duolm_packed_size(C.byref(p.tpl), p.reqs, p.n, C.byref(n)))
+    _check(lib().duolm_packed_size(C.byref(p.tpl), ptr, count, C.byref(n)))
     return n.value
 
 
-def duolm_pack_requests(p: PackInput, n_threads: int = 1, ids: np.ndarray | None = None):
-    """Returns (ids, prefix_len, n_cand, cand_len) as int32 arrays; `ids` may be
-    a caller buffer (for instance page-locked) of at least the packed size."""
+def duolm_pack_requests(p: PackInput, n_threads: int = 1, ids: np.ndarray | None = None, start: int = 0,
+                        count: int | None = None):
+    """Pack requests start .. start+count-1 of p.  Returns (ids, prefix_len,
+    n_cand, cand_len) as int32 arrays; `ids` may be a caller buffer of at least
+    the packed size (the returned ids are then a view of its first part)."""
+    ptr, count = _slice(p, start, count)
     if ids is None:
-        ids = np.empty(duolm_packed_size(p), dtype=np.int32)
-    L, K, M = (np.empty(p.n, dtype=np.int32) for _ in range(3))
-    _check(lib().duolm_pack_requests(C.byref(p.tpl), p.reqs, p.n, n_threads, ids.ctypes.data, ids.size,
+        ids = np.empty(duolm_packed_size(p, start, count), dtype=np.int32)
+    L, K, M = (np.empty(count, dtype=np.int32) for _ in range(3))
+    _check(lib().duolm_pack_requests(C.byref(p.tpl), ptr, count, n_threads, ids.ctypes.data, ids.size,
                                      L.ctypes.data, K.ctypes.data, M.ctypes.data))
-    return ids, L, K, M
+    return ids[:int(L.sum()) + int((K * M).sum())], L, K, M
 
 
 def duolm_score_packed(r, prefix_len, n_cand, cand_len, ids, mode: int = DUOLM_MODE_MIS, use_graph: bool = True,

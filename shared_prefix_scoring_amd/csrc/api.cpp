@@ -1209,7 +1209,10 @@ int duolm_pack_requests(const duolm_template* t, const duolm_history* reqs, int3
       cand_len[i] = std::max(reqs[i].cand_len, 1);
     }
   };
-  const int nt = std::min({std::max(n_threads, 1), (int)n_req, 64});
+  // a thread costs tens of microseconds to start, about what copying 64k ids
+  // takes: never more threads than 64k-id shares of the work
+  const int by_work = (int)std::min<int64_t>(64, total / 65536 + 1);
+  const int nt = std::min({std::max(n_threads, 1), (int)n_req, by_work});
   if (nt == 1) {
     work(0, n_req);
     return DUOLM_OK;

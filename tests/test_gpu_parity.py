@@ -339,3 +339,40 @@ def test_multivector_device_entry_and_errors(gpu_tiny):
         assert e.value.status == "EINVAL"
     with pytest.raises(ValueError):
         r.score([(p, c[:3])], cand_len=2)
+
+
+def _pack(reqs_full, cid, cfg, header=()):
+    marker, instr = synth.template(cid, cfg)
+    return spa.PackInput(instr, marker, [(r.items, r.feedback, r.cands, r.m, r.m) for r in reqs_full], header)
+
+
+def test_packed_host_path_matches_request_path(gpu_qwen, gpu_tiny):
+    # structured requests -> host packer -> pinned staging -> scores equal, bit
+    # for bit, to scoring the same requests given as flat id arrays
+    cfg, _, _, _, r = gpu_qwen
+    for cid, n in ((3, 64), (6, 16)):
+        full = synth.make_requests(cid, cfg, n_requests=n)
+        p = _pack(full, cid, cfg)
+        for nt in (1, 4):
+            ids, L, K, M = spa.duolm_pack_requests(p, n_threads=nt)
+            got = r.score_packed(L, K, M, ids)
+            want = r.score([(q.prefix, q.cands) for q in full], cand_len=[q.m for q in full])
+            np.testing.assert_array_equal(got, want)
+    # staging grows and shrinks across calls; a small call after a large one
+    tcfg, _, _, model, rt = gpu_tiny
+    small = synth.make_requests(1, tcfg)
+    ps = _pack(small, 1, tcfg)
+    ids, L, K, M = spa.duolm_pack_requests(ps)
+    np.testing.assert_array_equal(rt.score_packed(L, K, M, ids), rt.score([(q.prefix, q.cands) for q in small]))
+    check_against_oracle(model, [(q.prefix, q.cands) for q in small], rt.score_packed(L, K, M, ids))
+    # a candidate header is just trailing prefix ids
+    ph = _pack(small, 1, tcfg, header=(3, 4))
+    ids, L, K, M = spa.duolm_pack_requests(ph)
+    want = rt.score([(np.concatenate([q.prefix, [3, 4]]).astype(np.int32), q.cands) for q in small])
+    np.testing.assert_array_equal(rt.score_packed(L, K, M, ids), want)
+    # ids are range-checked on the way into the staging buffer
+    bad = ids.copy()
+    bad[5] = tcfg.vocab + tcfg.n_vid
+    with pytest.raises(spa.DuolmError) as ei:
+        rt.score_packed(L, K, M, bad)
+    assert ei.value.code == -2

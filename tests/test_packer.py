@@ -34,6 +34,18 @@ def test_packer_matches_oracle(cid, cfg, n):
                 np.testing.assert_array_equal(g, w)
 
 
+def test_packer_many_threads_large_batch():
+    # enough ids (about 2.4M) that the work cap allows many threads
+    cfg = synth.QWEN3_0P6B
+    reqs = synth.make_requests(3, cfg, n_requests=10_000)
+    marker, instr = synth.template(3, cfg)
+    p = pack_input(reqs, marker, instr)
+    want = expected(reqs, marker, instr)
+    for nt in (1, 7, 64):
+        for g, w in zip(spa.duolm_pack_requests(p, n_threads=nt), want):
+            np.testing.assert_array_equal(g, w)
+
+
 def test_packer_edge_shapes():
     # no history, empty feedback, multi-vector history with single-vector candidates
     reqs = [synth.Request(prefix=None, cands=np.array([900, 901], np.int32), m=1,
