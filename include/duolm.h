@@ -267,6 +267,63 @@ int duolm_pack_requests(const duolm_template* t, const duolm_history* reqs, int3
 int duolm_score_packed(duolm_ranker* r, const int32_t* prefix_len, const int32_t* n_cand, const int32_t* cand_len,
                        int32_t n_req, const int32_t* ids, float* scores, const duolm_opts* opts);
 
+/*
+ * Sessions: a user's prefix whose K and V stay on the GPU between calls, so
+ * that a newly arrived history item appends its rows' K and V instead of the
+ * whole prefix being prefilled again -- the pages' in-session incremental
+ * personalisation ([digest] 未来方向 (3): only the new item's vectors and KV
+ * are appended).  With causal attention the rows already computed do not
+ * depend on later rows, so appending is exact: a session's scores are, bit
+ * for bit, those of scoring its whole prefix in one call (same kernels, same
+ * reduction order).  Sharing one item's KV across different users' prefixes
+ * (未来方向 (5)) would change results and is not offered.
+ *
+ * K and V live in a pool of pages of 64 prefix rows x all layers
+ * (2 * n_layers * 64 * n_kv_heads * head_dim bf16 values per page: 7.3 MB
+ * for the 0.6B shape), reserved once per handle; sessions take pages as they
+ * grow and return them when freed.
+ */
+typedef struct duolm_session duolm_session; /* opaque, owned by the library */
+
+/* Reserve the pool for max_rows prefix rows in total over all sessions (in
+ * pages of 64).  Replaces an earlier pool; fails with ESTATE while sessions
+ * exist.  Errors: EINVAL, ENOMEM, ESTATE, EHIP. */
+int duolm_kv_pool_init(duolm_ranker* r, int64_t max_rows);
+
+/* Pages of the pool not held by any session. */
+int duolm_kv_pool_free_pages(const duolm_ranker* r, int64_t* n_free);
+
+/* A new empty session (prefix length 0).  Errors: EINVAL, ESTATE (no pool). */
+int duolm_session_create(duolm_ranker* r, duolm_session** out);
+
+/* Prefix rows the session holds. */
+int duolm_session_length(const duolm_session* s, int32_t* prefix_len);
+
+/* Returns the session's pages to the pool and frees it.  NULL is a no-op.
+ * Sessions still alive when their ranker is freed are freed with it. */
+void duolm_session_free(duolm_session* s);
+
+/*
+ * One call over n distinct sessions of this ranker.  Session i first appends
+ * n_new[i] prefix ids (at positions L_i .. L_i + n_new[i] - 1, attending to
+ * its cached rows and causally among themselves), then scores n_cand[i]
+ * candidates (0: none) of cand_len[i] ids each against its whole prefix,
+ * exactly as duolm_score_batch scores a request whose prefix is everything
+ * the session has appended so far.
+ *   ids    : host, per session [new ids, candidate ids], sessions in order.
+ *   scores : host, sum(n_cand) floats, session-major, candidates in order
+ *            (may be NULL when no candidates are scored).
+ *   cand_len : host array or NULL, as in duolm_request.
+ * On success each session's length grows by n_new[i]; on error no session
+ * length changes.  MIS mode only.  Synchronous.
+ * Errors: EINVAL (bad counts, a session twice or of another ranker, prefix
+ * over the maximum, candidates with an empty prefix), ERANGE, ESTATE,
+ * ENOMEM (the pool has too few free pages), EHIP.
+ */
+int duolm_session_step(duolm_ranker* r, duolm_session* const* sessions, int32_t n, const int32_t* n_new,
+                       const int32_t* n_cand, const int32_t* cand_len, const int32_t* ids, float* scores,
+                       const duolm_opts* opts);
+
 /* Kernel classes for the profiling counters. */
 typedef enum {
   DUOLM_K_EMBED = 0,      /* VID-aware embedding gather */

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     DuolmError,
     PackInput,
     Ranker,
+    Session,
     duolm_copy_device,
     duolm_debug_forward,
     duolm_debug_gemm,
@@ -36,6 +37,12 @@ from ._lib import (  # noqa: F401
     duolm_score_batch,
     duolm_score_batch_dev,
     duolm_score_packed,
+    duolm_session_create,
+    duolm_session_free,
+    duolm_session_length,
+    duolm_session_step,
+    duolm_kv_pool_free_pages,
+    duolm_kv_pool_init,
     duolm_set_profiling,
     lib,
 )

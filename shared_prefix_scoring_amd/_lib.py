@@ -5,6 +5,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import weakref
 from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
@@ -100,6 +101,13 @@ EXPORTS = {
                                       C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
     "duolm_score_packed": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
                                      C.c_void_p, C.POINTER(duolm_opts)]),
+    "duolm_kv_pool_init": (C.c_int, [C.c_void_p, C.c_int64]),
+    "duolm_kv_pool_free_pages": (C.c_int, [C.c_void_p, C.POINTER(C.c_int64)]),
+    "duolm_session_create": (C.c_int, [C.c_void_p, C.POINTER(C.c_void_p)]),
+    "duolm_session_length": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
+    "duolm_session_free": (None, [C.c_void_p]),
+    "duolm_session_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_void_p, C.c_void_p, C.POINTER(duolm_opts)]),
 }
 
 DUOLM_DTYPE_F32, DUOLM_DTYPE_BF16, DUOLM_DTYPE_F16 = 0, 1, 2
@@ -343,7 +351,76 @@ def duolm_score_packed(r, prefix_len, n_cand, cand_len, ids, mode: int = DUOLM_M
     return out
 
 
+def duolm_kv_pool_init(r, max_rows: int) -> None:
+    _check(lib().duolm_kv_pool_init(r, max_rows))
+
+
+def duolm_kv_pool_free_pages(r) -> int:
+    n = C.c_int64()
+    _check(lib().duolm_kv_pool_free_pages(r, C.byref(n)))
+    return n.value
+
+
+def duolm_session_create(r) -> C.c_void_p:
+    h = C.c_void_p()
+    _check(lib().duolm_session_create(r, C.byref(h)))
+    return h
+
+
+def duolm_session_length(s) -> int:
+    n = C.c_int32()
+    _check(lib().duolm_session_length(s, C.byref(n)))
+    return n.value
+
+
+def duolm_session_free(s) -> None:
+    lib().duolm_session_free(s)
+
+
+def duolm_session_step(r, sessions, new_ids, cands=None, cand_len=None, mode: int = DUOLM_MODE_MIS,
+                       use_graph: bool = True, stream=None) -> np.ndarray:
+    """sessions: handles; new_ids[i]: ids appended to session i (may be empty);
+    cands[i]: its candidate ids (empty or None: none), cand_len as in score()."""
+    n = len(sessions)
+    cands = [None] * n if cands is None else cands
+    M = _cand_lens(n, cand_len)
+    m = np.maximum(M, 1)
+    new = [np.asarray(x if x is not None else [], dtype=np.int32).reshape(-1) for x in new_ids]
+    cc = [np.asarray(x if x is not None else [], dtype=np.int32).reshape(-1) for x in cands]
+    n_new = np.array([x.size for x in new], dtype=np.int32)
+    n_cand = np.array([c.size // mi for c, mi in zip(cc, m)], dtype=np.int32)
+    parts = [a for pair in zip(new, cc) for a in pair]
+    ids = np.ascontiguousarray(np.concatenate(parts) if parts else np.zeros(0, np.int32), dtype=np.int32)
+    hs = (C.c_void_p * n)(*[s.value if isinstance(s, C.c_void_p) else s for s in sessions])
+    out = np.empty(int(n_cand.sum()), dtype=np.float32)
+    o = _opts(mode, use_graph, stream)
+    _check(lib().duolm_session_step(r, hs, n, n_new.ctypes.data, n_cand.ctypes.data,
+                                    None if cand_len is None else M.ctypes.data,
+                                    ids.ctypes.data if ids.size else None, out.ctypes.data if out.size else None,
+                                    C.byref(o)))
+    return out
+
+
 # ----------------------------------------------------------------- convenience
+
+class Session:
+    """Owning wrapper around a session handle (freed with close() or with its ranker)."""
+
+    def __init__(self, ranker: "Ranker"):
+        self.ranker = ranker
+        self.h = duolm_session_create(ranker.h)
+        ranker._sessions.add(self)
+
+    @property
+    def length(self) -> int:
+        return duolm_session_length(self.h)
+
+    def close(self) -> None:
+        if self.h:
+            duolm_session_free(self.h)
+            self.h = None
+            self.ranker._sessions.discard(self)
+
 
 class Ranker:
     """Owning wrapper around a ranker handle."""
@@ -351,6 +428,7 @@ class Ranker:
     def __init__(self, handle):
         self.h = handle
         self.dims = duolm_get_dims(handle)
+        self._sessions = weakref.WeakSet()
 
     @classmethod
     def from_file(cls, path: str, device: int = 0) -> "Ranker":
@@ -409,8 +487,25 @@ class Ranker:
     def kernel_stats(self, cls: str) -> duolm_kernel_stats:
         return duolm_get_kernel_stats(self.h, KERNEL_CLASSES.index(cls))
 
+    def kv_pool_init(self, max_rows: int) -> None:
+        duolm_kv_pool_init(self.h, max_rows)
+
+    def kv_free_pages(self) -> int:
+        return duolm_kv_pool_free_pages(self.h)
+
+    def session(self) -> Session:
+        return Session(self)
+
+    def step(self, sessions, new_ids, cands=None, cand_len=None, use_graph: bool = True, stream=None,
+             mode: int = DUOLM_MODE_MIS) -> np.ndarray:
+        return duolm_session_step(self.h, [x.h for x in sessions], new_ids, cands, cand_len, mode, use_graph,
+                                  stream)
+
     def close(self) -> None:
         if self.h:
+            for x in list(self._sessions):  # the library frees them with the ranker
+                x.h = None
+            self._sessions = weakref.WeakSet()
             duolm_free_ranker(self.h)
             self.h = None
 

@@ -27,6 +27,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <set>
 #include <string>
 #include <thread>
 #include <tuple>
@@ -91,13 +92,17 @@ struct Plan {
   std::vector<SeqDesc> seqs;
   std::vector<WorkItem> pitems, bitems;
   std::vector<int32_t> head_rows;
+  std::vector<int32_t> pages;   // page tables of session sequences
+  std::vector<int32_t> cached;  // per sequence: prefix rows computed by earlier calls
   int score_off = 0;
+  bool session = false;
 };
 
 struct Caps {
-  int T, seq, pitems, bitems, scores;
+  int T, seq, pitems, bitems, scores, pages, session;
   bool operator<(const Caps& o) const {
-    return std::tie(T, seq, pitems, bitems, scores) < std::tie(o.T, o.seq, o.pitems, o.bitems, o.scores);
+    return std::tie(T, seq, pitems, bitems, scores, pages, session) <
+           std::tie(o.T, o.seq, o.pitems, o.bitems, o.scores, o.pages, o.session);
   }
 };
 
@@ -157,9 +162,15 @@ struct duolm_ranker {
   int32_t* h_err = nullptr;  // pinned
   char* h_stage = nullptr;   // pinned staging for host ids in and host scores out
   size_t cap_stage = 0;
+  // session KV pool: kv_pages pages of kPageRows prefix rows, all layers
+  uint16_t* kv_pool = nullptr;
+  int64_t kv_pages = 0;
+  int64_t page_elems = 0;
+  std::vector<int32_t> kv_free;  // free page indices (a stack)
+  std::set<duolm_session*> sessions;
   // descriptor block
-  int cap_seq = 0, cap_pi = 0, cap_bi = 0, cap_hs = 0;
-  size_t off_sro = 0, off_seq = 0, off_pi = 0, off_bi = 0, off_hr = 0, meta_bytes = 0;
+  int cap_seq = 0, cap_pi = 0, cap_bi = 0, cap_hs = 0, cap_pt = 0;
+  size_t off_sro = 0, off_seq = 0, off_pi = 0, off_bi = 0, off_hr = 0, off_pt = 0, meta_bytes = 0;
   char* d_meta = nullptr;
   char* h_meta[2] = {nullptr, nullptr};
   hipEvent_t meta_free[2] = {nullptr, nullptr};
@@ -171,6 +182,14 @@ struct duolm_ranker {
   duolm_kernel_stats stats[DUOLM_K_COUNT]{};
   std::vector<hipEvent_t> ev_pool;
   size_t ev_used = 0;
+};
+
+// A user session: a prefix whose K and V stay in the ranker's KV pool between
+// calls, so new history rows are appended without recomputing the old ones.
+struct duolm_session {
+  duolm_ranker* owner;
+  int32_t L = 0;               // prefix rows computed so far
+  std::vector<int32_t> pages;  // page i holds rows [i kPageRows, (i + 1) kPageRows)
 };
 
 namespace {
@@ -403,8 +422,9 @@ int ensure_rows(duolm_ranker* R, int T) {
   return DUOLM_OK;
 }
 
-int ensure_meta(duolm_ranker* R, int n_seq, int n_pi, int n_bi, int n_hs) {
-  if (n_seq <= R->cap_seq && n_pi <= R->cap_pi && n_bi <= R->cap_bi && n_hs <= R->cap_hs) return DUOLM_OK;
+int ensure_meta(duolm_ranker* R, int n_seq, int n_pi, int n_bi, int n_hs, int n_pt) {
+  if (n_seq <= R->cap_seq && n_pi <= R->cap_pi && n_bi <= R->cap_bi && n_hs <= R->cap_hs && n_pt <= R->cap_pt)
+    return DUOLM_OK;
   HIP_TRY(hipStreamSynchronize(R->stream));
   drop_graphs(R);
   auto grow = [](int need, int have) { return std::max(have, std::max(256, (int)align_up((size_t)need * 5 / 4, 256))); };
@@ -412,12 +432,14 @@ int ensure_meta(duolm_ranker* R, int n_seq, int n_pi, int n_bi, int n_hs) {
   R->cap_pi = grow(n_pi, R->cap_pi);
   R->cap_bi = grow(n_bi, R->cap_bi);
   R->cap_hs = grow(n_hs, R->cap_hs);
+  R->cap_pt = grow(n_pt, R->cap_pt);
   size_t off = align_up(sizeof(CallHeader), 256);
   R->off_sro = off; off = align_up(off + (size_t)(R->cap_seq + 1) * 4, 256);
   R->off_seq = off; off = align_up(off + (size_t)R->cap_seq * sizeof(SeqDesc), 256);
   R->off_pi = off; off = align_up(off + (size_t)R->cap_pi * sizeof(WorkItem), 256);
   R->off_bi = off; off = align_up(off + (size_t)R->cap_bi * sizeof(WorkItem), 256);
   R->off_hr = off; off = align_up(off + (size_t)R->cap_hs * 4, 256);
+  R->off_pt = off; off = align_up(off + (size_t)R->cap_pt * 4, 256);
   R->meta_bytes = off;
   if (R->d_meta) (void)hipFree(R->d_meta);
   for (auto& h : R->h_meta)
@@ -426,7 +448,7 @@ int ensure_meta(duolm_ranker* R, int n_seq, int n_pi, int n_bi, int n_hs) {
   R->h_meta[0] = R->h_meta[1] = nullptr;
   if (hipMalloc((void**)&R->d_meta, off) != hipSuccess || hipHostMalloc((void**)&R->h_meta[0], off) != hipSuccess ||
       hipHostMalloc((void**)&R->h_meta[1], off) != hipSuccess) {
-    R->cap_seq = R->cap_pi = R->cap_bi = R->cap_hs = 0;
+    R->cap_seq = R->cap_pi = R->cap_bi = R->cap_hs = R->cap_pt = 0;
     return fail(DUOLM_ENOMEM, "descriptor buffers (%zu bytes)", off);
   }
   return DUOLM_OK;
@@ -457,6 +479,9 @@ DevBatch dev_batch(duolm_ranker* R) {
   b.bitems = (const WorkItem*)(R->d_meta + R->off_bi);
   b.head_rows = (const int32_t*)(R->d_meta + R->off_hr);
   b.err = R->d_err;
+  b.pages = (const int32_t*)(R->d_meta + R->off_pt);
+  b.kv = R->kv_pool;
+  b.page_stride = R->page_elems;
   return b;
 }
 
@@ -477,15 +502,50 @@ void plan_add_seq(duolm_ranker* R, Plan& P, int L, int K, int M, int id_off, int
   sd.id_len = id_len;
   sd.cand_id_off = cand_id_off;
   sd.M = M;
+  sd.pt = -1;
   P.seqs.push_back(sd);
+  P.cached.push_back(0);
   P.seq_row_off.push_back(P.T);
   const int rp = attn_rows_per_item(false, G);
   const int rb = attn_rows_per_item(true, G) / M * M;  // whole branches per tile
   const int KM = K * M;
-  for (int r0 = 0; r0 < L; r0 += rp) P.pitems.push_back({s, r0, P.T, L, KM, M, {0, 0}});
-  for (int c0 = 0; c0 < KM; c0 += rb) P.bitems.push_back({s, c0, P.T, L, KM, M, {0, 0}});
+  for (int r0 = 0; r0 < L; r0 += rp) P.pitems.push_back({s, r0, P.T, L, KM, M, -1, 0});
+  for (int c0 = 0; c0 < KM; c0 += rb) P.bitems.push_back({s, c0, P.T, L, KM, M, -1, 0});
   for (int j = 0; j < K; ++j) P.head_rows.push_back(P.T + L + j * M + M - 1);
   P.T += L + KM;
+}
+
+// A session sequence: prefix rows [0, Lc) were computed by earlier calls (their
+// K and V are in the session's pages), rows [Lc, L) are new, then K branches.
+// Only the new rows and the branches are packed; row_off and id_off are
+// virtual (row Lc sits at the packed position P.T).  ids: the new prefix ids
+// at new_id_off, the candidates' at cand_id_off.
+void plan_add_session(duolm_ranker* R, Plan& P, int Lc, int L, int K, int M, int new_id_off, int cand_id_off,
+                      const std::vector<int32_t>& pages) {
+  const int G = R->dims.n_heads / R->dims.n_kv_heads;
+  const int s = (int)P.seqs.size();
+  const int voff = P.T - Lc;
+  SeqDesc sd{};
+  sd.row_off = voff;
+  sd.L = L;
+  sd.K = K;
+  sd.id_off = new_id_off - Lc;
+  sd.id_len = L;
+  sd.cand_id_off = cand_id_off;
+  sd.M = M;
+  sd.pt = (int)P.pages.size();
+  P.pages.insert(P.pages.end(), pages.begin(), pages.begin() + (L + kPageRows - 1) / kPageRows);
+  P.seqs.push_back(sd);
+  P.cached.push_back(Lc);
+  P.seq_row_off.push_back(P.T);
+  const int rp = attn_rows_per_item(false, G);
+  const int rb = attn_rows_per_item(true, G) / M * M;
+  const int KM = K * M;
+  for (int r0 = Lc; r0 < L; r0 += rp) P.pitems.push_back({s, r0, voff, L, KM, M, sd.pt, 0});
+  for (int c0 = 0; c0 < KM; c0 += rb) P.bitems.push_back({s, c0, voff, L, KM, M, sd.pt, 0});
+  for (int j = 0; j < K; ++j) P.head_rows.push_back(P.T + (L - Lc) + j * M + M - 1);
+  P.T += (L - Lc) + KM;
+  P.session = true;
 }
 
 // Close a launch: attention tiles go longest first (their key count is the
@@ -519,10 +579,12 @@ void launch_work(const duolm_ranker* R, const Plan& P, double fl[DUOLM_K_COUNT],
   by[DUOLM_K_GEMM_GATEUP] = (2 * F * d + T * d + T * F) * 2;
   fl[DUOLM_K_GEMM_DOWN] = 2 * T * F * d;
   by[DUOLM_K_GEMM_DOWN] = (d * F + T * F) * 2 + T * d * 8;
-  for (const SeqDesc& s : P.seqs) {
-    const double L = s.L, K = s.K, M = s.M;
-    fl[DUOLM_K_ATTN_PREFIX] += 4 * hd * H * L * (L + 1) / 2;
-    by[DUOLM_K_ATTN_PREFIX] += L * (H * hd * 2 + Hk * hd * 4 + H * hd * 2);
+  for (size_t i = 0; i < P.seqs.size(); ++i) {
+    const SeqDesc& s = P.seqs[i];
+    const double L = s.L, K = s.K, M = s.M, Lc = P.cached[i];
+    // new causal rows r = Lc .. L - 1 see r + 1 keys; cached rows' K/V come from pages
+    fl[DUOLM_K_ATTN_PREFIX] += 4 * hd * H * (L * (L + 1) - Lc * (Lc + 1)) / 2;
+    if (L > Lc) by[DUOLM_K_ATTN_PREFIX] += (L - Lc) * (H * hd * 2 + Hk * hd * 4 + H * hd * 2) + Lc * Hk * hd * 4;
     // branch row i sees L prefix keys and i + 1 keys of its own branch
     fl[DUOLM_K_ATTN_BRANCH] += 4 * hd * H * K * (M * L + M * (M + 1) / 2);
     if (K > 0) by[DUOLM_K_ATTN_BRANCH] += L * Hk * hd * 4 + K * M * (H * hd * 2 + Hk * hd * 4 + H * hd * 2);
@@ -608,6 +670,8 @@ void enqueue_forward(Enq& q, const Caps& c) {
   if (q.stop(0, DUOLM_STAGE_EMBED)) return;
   for (int l = 0; l < D.n_layers; ++l) {
     const LayerW& W = R->layers[l];
+    DevBatch bl = b;  // this layer's block of the session KV pages
+    if (R->kv_pool) bl.kv = R->kv_pool + (size_t)l * 2 * kPageRows * Hk * hd;
     q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, c.T, R->X, W.attn_norm, R->Xn, b.hdr, d, eps); });
     if (q.stop(l, DUOLM_STAGE_ATTN_NORM)) return;
     q.run(DUOLM_K_GEMM_QKV, [&] { launch_gemm(s, EPI_BF16, c.T, R->Xn, d, W.wqkv, d, R->QKV, nq, dT, nq, d); });
@@ -616,11 +680,12 @@ void enqueue_forward(Enq& q, const Caps& c) {
       launch_qk_rope(s, c.T, R->QKV, nq, b.hdr, R->pos, W.q_norm, W.k_norm, R->rope, H, Hk, hd, eps);
     });
     if (q.stop(l, DUOLM_STAGE_QK_ROPE)) return;
+    if (c.session) launch_kv_store(s, c.T, R->QKV, nq, bl, H, Hk, hd);
     q.run(DUOLM_K_ATTN_PREFIX,
-          [&] { launch_attn(s, false, hd, c.pitems, R->QKV, nq, R->Ob, H * hd, b, H, Hk, scale_log2); });
+          [&] { launch_attn(s, false, hd, c.pitems, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
     if (c.bitems > 0)
       q.run(DUOLM_K_ATTN_BRANCH,
-            [&] { launch_attn(s, true, hd, c.bitems, R->QKV, nq, R->Ob, H * hd, b, H, Hk, scale_log2); });
+            [&] { launch_attn(s, true, hd, c.bitems, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
     if (q.stop(l, DUOLM_STAGE_ATTN)) return;
     q.run(DUOLM_K_GEMM_O, [&] { launch_gemm(s, EPI_RESID, c.T, R->Ob, H * hd, W.wo, H * hd, R->X, d, dT, d, H * hd); });
     if (q.stop(l, DUOLM_STAGE_ATTN_RESID)) return;
@@ -655,17 +720,18 @@ int upload_plan(duolm_ranker* R, const Plan& P, hipStream_t s) {
   memcpy(h + R->off_pi, P.pitems.data(), P.pitems.size() * sizeof(WorkItem));
   memcpy(h + R->off_bi, P.bitems.data(), P.bitems.size() * sizeof(WorkItem));
   memcpy(h + R->off_hr, P.head_rows.data(), P.head_rows.size() * 4);
+  if (!P.pages.empty()) memcpy(h + R->off_pt, P.pages.data(), P.pages.size() * 4);
   // copy up to the end of the last used section in one transfer when the gaps
   // are small, else section by section
-  const size_t end_hr = R->off_hr + P.head_rows.size() * 4;
-  if (end_hr <= 256 * 1024) {
-    HIP_TRY(hipMemcpyAsync(R->d_meta, h, end_hr, hipMemcpyHostToDevice, s));
+  const size_t end_used = P.pages.empty() ? R->off_hr + P.head_rows.size() * 4 : R->off_pt + P.pages.size() * 4;
+  if (end_used <= 256 * 1024) {
+    HIP_TRY(hipMemcpyAsync(R->d_meta, h, end_used, hipMemcpyHostToDevice, s));
   } else {
-    const size_t offs[6] = {0, R->off_sro, R->off_seq, R->off_pi, R->off_bi, R->off_hr};
-    const size_t lens[6] = {sizeof(CallHeader), P.seq_row_off.size() * 4, P.seqs.size() * sizeof(SeqDesc),
+    const size_t offs[7] = {0, R->off_sro, R->off_seq, R->off_pi, R->off_bi, R->off_hr, R->off_pt};
+    const size_t lens[7] = {sizeof(CallHeader), P.seq_row_off.size() * 4, P.seqs.size() * sizeof(SeqDesc),
                             P.pitems.size() * sizeof(WorkItem), P.bitems.size() * sizeof(WorkItem),
-                            P.head_rows.size() * 4};
-    for (int i = 0; i < 6; ++i)
+                            P.head_rows.size() * 4, P.pages.size() * 4};
+    for (int i = 0; i < 7; ++i)
       if (lens[i]) HIP_TRY(hipMemcpyAsync(R->d_meta + offs[i], h + offs[i], lens[i], hipMemcpyHostToDevice, s));
   }
   HIP_TRY(hipEventRecord(R->meta_free[slot], s));
@@ -689,7 +755,8 @@ int run_launch(duolm_ranker* R, const Plan& P, hipStream_t s, bool use_graph, st
   int rc = upload_plan(R, P, s);
   if (rc) return rc;
   if (!use_graph) {
-    Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size()};
+    Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(),
+           (int)P.pages.size(), P.session ? 1 : 0};
     Enq q{R, s, R->prof_mask ? timed : nullptr, nullptr};
     enqueue_forward(q, c);
     HIP_TRY(hipGetLastError());
@@ -697,7 +764,7 @@ int run_launch(duolm_ranker* R, const Plan& P, hipStream_t s, bool use_graph, st
   }
   Caps c{std::min(bucket(P.T), R->cap_T), std::min(bucket((int)P.seqs.size()), R->cap_seq),
          std::min(bucket((int)P.pitems.size()), R->cap_pi), std::min(bucket((int)P.bitems.size()), R->cap_bi),
-         std::min(bucket((int)P.head_rows.size()), R->cap_hs)};
+         std::min(bucket((int)P.head_rows.size()), R->cap_hs), 0, P.session ? 1 : 0};
   auto it = R->graphs.find(c);
   if (it == R->graphs.end()) {
     GraphEntry ge;
@@ -819,58 +886,50 @@ int mode_ok(const duolm_opts* o) {
   return DUOLM_OK;
 }
 
-// Shared body of the host and device entry points.  `ids` is host memory
-// when ids_dev is false.  Scores go to `out` (host or device).
-int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool ids_dev, float* out, bool out_dev,
-               const duolm_opts* opts, const uint16_t* inline_rows = nullptr, int64_t n_inline = 0) {
-  if (!R || !in.prefix_len || !in.n_cand || !ids || !out) return fail(DUOLM_EINVAL, "NULL argument");
-  int rc = mode_ok(opts);
-  if (rc) return rc;
-  const int mode = opts ? opts->mode : DUOLM_MODE_MIS;
-  const bool use_graph = opts ? opts->use_graph != 0 : true;
-  hipStream_t s = (opts && opts->hip_stream) ? (hipStream_t)opts->hip_stream : R->stream;
-  int64_t total_ids = 0, total_scores = 0;
-  rc = validate_lengths(R, in, total_ids, total_scores);
-  if (rc) return rc;
-  HIP_TRY(hipSetDevice(R->device));
-  const bool stage = !ids_dev || !out_dev;
-  if (stage && (rc = ensure_stage(R, (size_t)std::max(total_ids, total_scores) * 4))) return rc;
-  if (!ids_dev) {
-    // range-check the host ids while copying them into the pinned stage
-    const int64_t lim = (int64_t)R->dims.vocab + R->n_vid + n_inline;
-    int32_t* st = (int32_t*)R->h_stage;
-    for (int64_t i = 0; i < total_ids; ++i) {
-      const int32_t id = ids[i];
-      if (id < 0 || id >= lim) {
-        if (id >= R->dims.vocab && R->n_vid + n_inline == 0 && id >= 0)
-          return fail(DUOLM_ESTATE, "id %d at position %lld is a VID but no item table is loaded", id, (long long)i);
-        return fail(DUOLM_ERANGE, "id %d at position %lld outside [0, %lld)", id, (long long)i, (long long)lim);
-      }
-      st[i] = id;
+// Range-check host ids while copying them into the pinned stage.
+int stage_host_ids(duolm_ranker* R, const int32_t* ids, int64_t total_ids, int64_t n_inline) {
+  const int64_t lim = (int64_t)R->dims.vocab + R->n_vid + n_inline;
+  int32_t* st = (int32_t*)R->h_stage;
+  for (int64_t i = 0; i < total_ids; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= lim) {
+      if (id >= R->dims.vocab && R->n_vid + n_inline == 0 && id >= 0)
+        return fail(DUOLM_ESTATE, "id %d at position %lld is a VID but no item table is loaded", id, (long long)i);
+      return fail(DUOLM_ERANGE, "id %d at position %lld outside [0, %lld)", id, (long long)i, (long long)lim);
     }
-    ids = st;
+    st[i] = id;
   }
-  std::vector<Plan> plans;
-  build_plans(R, in, mode, plans);
-  int maxT = 0, mseq = 0, mpi = 0, mbi = 0, mhs = 0;
+  return DUOLM_OK;
+}
+
+// Run planned launches: grow the buffers, upload the ids, launch every plan
+// (graph or eager), check the device id flag, return the scores.  `ids` is
+// the pinned stage or device memory (ids_dev).
+int run_plans(duolm_ranker* R, const std::vector<Plan>& plans, const int32_t* ids, bool ids_dev, int64_t total_ids,
+              float* out, bool out_dev, int64_t total_scores, hipStream_t s, bool use_graph,
+              const uint16_t* inline_rows = nullptr, int64_t n_inline = 0) {
+  int rc;
+  int maxT = 0, mseq = 0, mpi = 0, mbi = 0, mhs = 0, mpt = 0;
   for (const Plan& P : plans) {
     maxT = std::max(maxT, P.T);
     mseq = std::max(mseq, (int)P.seqs.size());
     mpi = std::max(mpi, (int)P.pitems.size());
     mbi = std::max(mbi, (int)P.bitems.size());
     mhs = std::max(mhs, (int)P.head_rows.size());
+    mpt = std::max(mpt, (int)P.pages.size());
   }
   if ((rc = ensure_rows(R, maxT))) return rc;
-  if ((rc = ensure_meta(R, mseq, mpi, mbi, mhs))) return rc;
-  if ((rc = ensure_buf(R, R->d_ids, R->cap_ids, total_ids))) return rc;
-  if ((rc = ensure_buf(R, R->d_out, R->cap_out, total_scores))) return rc;
+  if ((rc = ensure_meta(R, mseq, mpi, mbi, mhs, mpt))) return rc;
+  if ((rc = ensure_buf(R, R->d_ids, R->cap_ids, std::max<int64_t>(1, total_ids)))) return rc;
+  if ((rc = ensure_buf(R, R->d_out, R->cap_out, std::max<int64_t>(1, total_scores)))) return rc;
   if ((rc = ensure_buf(R, R->d_inline, R->cap_inline, std::max<int64_t>(1, n_inline) * R->dims.d_model))) return rc;
   if (s != R->stream) HIP_TRY(hipStreamSynchronize(R->stream));
   R->call_n_inline = (int32_t)n_inline;
   if (n_inline > 0)
     HIP_TRY(hipMemcpyAsync(R->d_inline, inline_rows, (size_t)n_inline * R->dims.d_model * 2, hipMemcpyHostToDevice, s));
-  HIP_TRY(hipMemcpyAsync(R->d_ids, ids, (size_t)total_ids * 4,
-                         ids_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s));
+  if (total_ids > 0)
+    HIP_TRY(hipMemcpyAsync(R->d_ids, ids, (size_t)total_ids * 4,
+                           ids_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s));
   *R->h_err = 0;
   HIP_TRY(hipMemcpyAsync(R->d_err, R->h_err, 4, hipMemcpyHostToDevice, s));
   R->ev_used = 0;
@@ -895,11 +954,39 @@ int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool id
     }
   }
   if (*R->h_err) return fail(DUOLM_ERANGE, "an id in the device batch is outside [0, V + N)");
-  HIP_TRY(hipMemcpyAsync(out_dev ? (void*)out : (void*)R->h_stage, R->d_out, (size_t)total_scores * 4,
-                         out_dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost, s));
-  HIP_TRY(hipStreamSynchronize(s));
-  if (!out_dev) memcpy(out, R->h_stage, (size_t)total_scores * 4);
+  if (total_scores > 0) {
+    HIP_TRY(hipMemcpyAsync(out_dev ? (void*)out : (void*)R->h_stage, R->d_out, (size_t)total_scores * 4,
+                           out_dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    if (!out_dev) memcpy(out, R->h_stage, (size_t)total_scores * 4);
+  }
   return DUOLM_OK;
+}
+
+// Shared body of the host and device entry points.  `ids` is host memory
+// when ids_dev is false.  Scores go to `out` (host or device).
+int score_impl(duolm_ranker* R, const CallInput& in, const int32_t* ids, bool ids_dev, float* out, bool out_dev,
+               const duolm_opts* opts, const uint16_t* inline_rows = nullptr, int64_t n_inline = 0) {
+  if (!R || !in.prefix_len || !in.n_cand || !ids || !out) return fail(DUOLM_EINVAL, "NULL argument");
+  int rc = mode_ok(opts);
+  if (rc) return rc;
+  const int mode = opts ? opts->mode : DUOLM_MODE_MIS;
+  const bool use_graph = opts ? opts->use_graph != 0 : true;
+  hipStream_t s = (opts && opts->hip_stream) ? (hipStream_t)opts->hip_stream : R->stream;
+  int64_t total_ids = 0, total_scores = 0;
+  rc = validate_lengths(R, in, total_ids, total_scores);
+  if (rc) return rc;
+  HIP_TRY(hipSetDevice(R->device));
+  if (!ids_dev || !out_dev) {
+    if ((rc = ensure_stage(R, (size_t)std::max(total_ids, total_scores) * 4))) return rc;
+  }
+  if (!ids_dev) {
+    if ((rc = stage_host_ids(R, ids, total_ids, n_inline))) return rc;
+    ids = (const int32_t*)R->h_stage;
+  }
+  std::vector<Plan> plans;
+  build_plans(R, in, mode, plans);
+  return run_plans(R, plans, ids, ids_dev, total_ids, out, out_dev, total_scores, s, use_graph, inline_rows, n_inline);
 }
 
 // Concatenate host requests as [prefix_0, cands_0, prefix_1, ...].  Requests
@@ -1240,6 +1327,137 @@ int duolm_score_packed(duolm_ranker* R, const int32_t* prefix_len, const int32_t
   return score_impl(R, in, ids, false, scores, false, opts);
 }
 
+// ---------------------------------------------------------------------------
+// sessions: prefix KV kept across calls
+// ---------------------------------------------------------------------------
+int duolm_kv_pool_init(duolm_ranker* R, int64_t max_rows) {
+  if (!R) return fail(DUOLM_EINVAL, "NULL argument");
+  if (max_rows < 1) return fail(DUOLM_EINVAL, "max_rows must be >= 1");
+  if (!R->sessions.empty()) return fail(DUOLM_ESTATE, "sessions still hold pages of the current pool");
+  const auto& D = R->dims;
+  const int64_t n_pages = (max_rows + kPageRows - 1) / kPageRows;
+  if (n_pages > INT32_MAX) return fail(DUOLM_EINVAL, "max_rows too large");
+  const int64_t page_elems = (int64_t)D.n_layers * 2 * kPageRows * D.n_kv_heads * D.head_dim;
+  HIP_TRY(hipSetDevice(R->device));
+  HIP_TRY(hipStreamSynchronize(R->stream));
+  uint16_t* p = nullptr;
+  const size_t bytes = (size_t)n_pages * page_elems * 2;
+  if (hipMalloc((void**)&p, bytes) != hipSuccess) return fail(DUOLM_ENOMEM, "KV pool (%zu bytes)", bytes);
+  if (R->kv_pool) (void)hipFree(R->kv_pool);
+  drop_graphs(R);  // graphs bake the pool address
+  R->kv_pool = p;
+  R->kv_pages = n_pages;
+  R->page_elems = page_elems;
+  R->kv_free.resize((size_t)n_pages);
+  for (int64_t i = 0; i < n_pages; ++i) R->kv_free[(size_t)i] = (int32_t)(n_pages - 1 - i);
+  return DUOLM_OK;
+}
+
+int duolm_kv_pool_free_pages(const duolm_ranker* R, int64_t* n_free) {
+  if (!R || !n_free) return fail(DUOLM_EINVAL, "NULL argument");
+  *n_free = (int64_t)R->kv_free.size();
+  return DUOLM_OK;
+}
+
+int duolm_session_create(duolm_ranker* R, duolm_session** out) {
+  if (!R || !out) return fail(DUOLM_EINVAL, "NULL argument");
+  if (!R->kv_pool) return fail(DUOLM_ESTATE, "no KV pool: call duolm_kv_pool_init first");
+  duolm_session* S = new duolm_session{R, 0, {}};
+  R->sessions.insert(S);
+  *out = S;
+  return DUOLM_OK;
+}
+
+int duolm_session_length(const duolm_session* S, int32_t* L) {
+  if (!S || !L) return fail(DUOLM_EINVAL, "NULL argument");
+  *L = S->L;
+  return DUOLM_OK;
+}
+
+void duolm_session_free(duolm_session* S) {
+  if (!S) return;
+  duolm_ranker* R = S->owner;
+  R->kv_free.insert(R->kv_free.end(), S->pages.rbegin(), S->pages.rend());
+  R->sessions.erase(S);
+  delete S;
+}
+
+int duolm_session_step(duolm_ranker* R, duolm_session* const* sess, int32_t n, const int32_t* n_new,
+                       const int32_t* n_cand, const int32_t* cand_len, const int32_t* ids, float* scores,
+                       const duolm_opts* opts) {
+  if (!R || !sess || !n_new || !n_cand || n < 1) return fail(DUOLM_EINVAL, "NULL argument or n < 1");
+  if (opts && opts->mode != DUOLM_MODE_MIS) return fail(DUOLM_EINVAL, "sessions score in MIS mode only");
+  const bool use_graph = opts ? opts->use_graph != 0 : true;
+  hipStream_t s = (opts && opts->hip_stream) ? (hipStream_t)opts->hip_stream : R->stream;
+  // validate everything before touching any session
+  std::set<const duolm_session*> seen;
+  int64_t total_ids = 0, total_scores = 0, need_pages = 0;
+  for (int i = 0; i < n; ++i) {
+    const duolm_session* S = sess[i];
+    if (!S || S->owner != R) return fail(DUOLM_EINVAL, "session %d is NULL or belongs to another ranker", i);
+    if (!seen.insert(S).second) return fail(DUOLM_EINVAL, "session %d appears twice", i);
+    if (n_new[i] < 0 || n_cand[i] < 0) return fail(DUOLM_EINVAL, "session %d: negative count", i);
+    if (cand_len && (cand_len[i] < 0 || cand_len[i] > max_cand_len(R)))
+      return fail(DUOLM_EINVAL, "session %d: cand_len %d outside [0, %d]", i, cand_len[i], max_cand_len(R));
+    const int m = cand_len && cand_len[i] > 1 ? cand_len[i] : 1;
+    const int64_t L = (int64_t)S->L + n_new[i];
+    if (n_cand[i] > 0 && L < 1) return fail(DUOLM_EINVAL, "session %d: candidates need a prefix", i);
+    if (L + m - 1 > R->dims.max_prefix)
+      return fail(DUOLM_EINVAL, "session %d: prefix %lld + cand_len %d over %d", i, (long long)L, m,
+                  R->dims.max_prefix + 1);
+    const int64_t rows = (int64_t)n_new[i] + (int64_t)n_cand[i] * m;
+    if (rows > R->max_rows)
+      return fail(DUOLM_EINVAL, "session %d: %lld rows over the %lld-row launch limit", i, (long long)rows,
+                  (long long)R->max_rows);
+    need_pages += std::max<int64_t>(0, (L + kPageRows - 1) / kPageRows - (int64_t)S->pages.size());
+    total_ids += rows;
+    total_scores += n_cand[i];
+  }
+  if (total_ids < 1) return fail(DUOLM_EINVAL, "nothing to compute");
+  if (total_ids > INT32_MAX / 2) return fail(DUOLM_EINVAL, "batch too large");
+  if (!ids || (total_scores > 0 && !scores)) return fail(DUOLM_EINVAL, "NULL ids or scores");
+  if (need_pages > (int64_t)R->kv_free.size())
+    return fail(DUOLM_ENOMEM, "KV pool: %lld pages needed, %lld free", (long long)need_pages,
+                (long long)R->kv_free.size());
+  HIP_TRY(hipSetDevice(R->device));
+  int rc = ensure_stage(R, (size_t)std::max(total_ids, total_scores) * 4);
+  if (rc) return rc;
+  if ((rc = stage_host_ids(R, ids, total_ids, 0))) return rc;
+  // pages for the new rows (a session keeps them if the call fails later:
+  // they lie past its length and the next append writes them again)
+  for (int i = 0; i < n; ++i) {
+    duolm_session* S = sess[i];
+    const int64_t want = ((int64_t)S->L + n_new[i] + kPageRows - 1) / kPageRows;
+    while ((int64_t)S->pages.size() < want) {
+      S->pages.push_back(R->kv_free.back());
+      R->kv_free.pop_back();
+    }
+  }
+  std::vector<Plan> plans(1);
+  int64_t off = 0;
+  int score = 0;
+  for (int i = 0; i < n; ++i) {
+    const duolm_session* S = sess[i];
+    const int m = cand_len && cand_len[i] > 1 ? cand_len[i] : 1;
+    const int rows = n_new[i] + n_cand[i] * m;
+    if (rows == 0) continue;
+    if (plans.back().T > 0 && plans.back().T + (int64_t)rows > R->max_rows) {
+      plan_close(R, plans.back());
+      plans.emplace_back();
+      plans.back().score_off = score;
+    }
+    plan_add_session(R, plans.back(), S->L, S->L + n_new[i], n_cand[i], m, (int)off, (int)(off + n_new[i]),
+                     S->pages);
+    off += rows;
+    score += n_cand[i];
+  }
+  plan_close(R, plans.back());
+  rc = run_plans(R, plans, (const int32_t*)R->h_stage, false, total_ids, scores, false, total_scores, s, use_graph);
+  if (rc) return rc;
+  for (int i = 0; i < n; ++i) sess[i]->L += n_new[i];
+  return DUOLM_OK;
+}
+
 int duolm_get_dims(const duolm_ranker* R, duolm_dims* out) {
   if (!R || !out) return fail(DUOLM_EINVAL, "NULL argument");
   *out = R->dims;
@@ -1299,6 +1517,8 @@ void duolm_free_ranker(duolm_ranker* R) {
   if (R->d_err) (void)hipFree(R->d_err);
   if (R->h_err) (void)hipHostFree(R->h_err);
   if (R->h_stage) (void)hipHostFree(R->h_stage);
+  for (duolm_session* S : R->sessions) delete S;
+  if (R->kv_pool) (void)hipFree(R->kv_pool);
   if (R->d_meta) (void)hipFree(R->d_meta);
   for (char* h : R->h_meta)
     if (h) (void)hipHostFree(h);
@@ -1345,7 +1565,8 @@ int duolm_debug_forward(duolm_ranker* R, const duolm_request* reqs, int32_t n_re
   if (nbytes != row_bytes * P.T) return fail(DUOLM_EINVAL, "nbytes %llu != %zu", (unsigned long long)nbytes, row_bytes * P.T);
   HIP_TRY(hipSetDevice(R->device));
   if ((rc = ensure_rows(R, P.T))) return rc;
-  if ((rc = ensure_meta(R, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size())))
+  if ((rc = ensure_meta(R, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(),
+                        (int)P.pages.size())))
     return rc;
   if ((rc = ensure_buf(R, R->d_ids, R->cap_ids, total_ids))) return rc;
   if ((rc = ensure_buf(R, R->d_out, R->cap_out, total_scores))) return rc;
@@ -1356,7 +1577,7 @@ int duolm_debug_forward(duolm_ranker* R, const duolm_request* reqs, int32_t n_re
   *R->h_err = 0;
   HIP_TRY(hipMemcpyAsync(R->d_err, R->h_err, 4, hipMemcpyHostToDevice, s));
   if ((rc = upload_plan(R, P, s))) return rc;
-  Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size()};
+  Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(), 0, 0};
   Enq q{R, s, nullptr, nullptr};
   q.stop_layer = layer == D.n_layers ? D.n_layers - 1 : layer;
   q.stop_stage = buf_stage;

@@ -18,6 +18,14 @@ namespace duolm {
 // (request, candidate) holding the prefix and that candidate alone (K = 1).
 // Row rho of a sequence takes its id from ids[id_off + rho] when rho < id_len,
 // else from ids[cand_id_off + rho - id_len].
+//
+// A session sequence continues a prefix whose first Lc rows were computed by
+// earlier calls: their K and V live in pages of the KV pool (page table at
+// pt), and only rows Lc .. of the sequence are packed.  row_off and id_off
+// are then virtual (the packed position of row Lc, minus Lc), so row rho is
+// still at row_off + rho; rows below Lc are never addressed in the packed
+// buffers.  The prefix keys of such a sequence are read from its pages, into
+// which the forward stores the K and V of its new prefix rows first.
 // ---------------------------------------------------------------------------
 struct SeqDesc {
   int32_t row_off;
@@ -27,7 +35,7 @@ struct SeqDesc {
   int32_t id_len;
   int32_t cand_id_off;
   int32_t M;       // rows per candidate branch (positions L .. L + M - 1)
-  int32_t pad1;
+  int32_t pt;      // session sequences: offset of the page table in DevBatch::pages; else -1
 };
 
 // A tile of query rows: prefix tiles start at row r0 of the sequence,
@@ -40,7 +48,8 @@ struct WorkItem {
   int32_t L;
   int32_t K;        // branch rows of the sequence (candidates x M)
   int32_t M;        // rows per candidate branch
-  int32_t pad[2];
+  int32_t pt;       // the sequence's page table offset (-1: prefix keys are rows of the packed QKV)
+  int32_t pad;
 };
 
 struct CallHeader {
@@ -56,6 +65,11 @@ struct CallHeader {
 static_assert(sizeof(CallHeader) == 64, "header layout");
 
 constexpr int kMaxPos = 32768;  // rotary table length; prefixes are shorter
+
+// Session KV pages: kPageRows consecutive prefix rows of one sequence, for
+// every layer: layer l holds K rows [kPageRows][Hkv * hd] then V rows, bf16.
+// A page is one key tile of the attention kernel.
+constexpr int kPageRows = 64;
 
 // ---------------------------------------------------------------------------
 // device helpers

@@ -86,6 +86,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   constexpr int TILE = BKV * HD;       // elements of one K or V tile
   constexpr int KB = BKV / 32;         // 32-key blocks per tile
   static_assert(BKV == 32 || BKV == 64, "key tile");
+  static_assert(kPageRows % BKV == 0, "a key tile lies in one session page");
   constexpr int QCH = NC * CPR;        // 16-byte chunks of the query block
   static_assert(QCH % (64 * NW) == 0, "staging layout");
   auto vswz = [](int key) { return vswz_t<CPR>(key); };
@@ -196,6 +197,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   // consecutive keys.  K chunk dc of key k sits at slot dc ^ (k % CPR), V chunk
   // dc at slot dc ^ vswz(k); each lane fetches the chunk that belongs at its
   // slot.  Keys past kend load key kend - 1 (valid memory, masked out).
+  // A tile's keys are consecutive rows of one source: rows of the packed QKV
+  // buffer, or, for a session sequence, rows of one KV page (a page holds
+  // kPageRows keys and tiles start at multiples of BKV, so a tile never
+  // straddles two pages).
   constexpr int KPI = 1024 / (2 * HD);        // keys per load instruction
   constexpr int NLI = BKV / KPI;              // instructions per tile and matrix
   constexpr int LPW = (2 * NLI + NW - 1) / NW;  // instructions per wave (K and V)
@@ -211,7 +216,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
         const int slot = lane % CPR;
         const int dc = slot ^ (isv ? vswz(key) : key % CPR);
         const int kr = min(k0 + key, kend - 1);
-        const uint16_t* src = seq_base + (size_t)kr * ld + (isv ? vcol : kcol) + dc * 8;
+        const uint16_t* src;
+        if (item.pt >= 0) {
+          const int pg = b.pages[item.pt + k0 / kPageRows];  // uniform over the tile
+          const uint16_t* page = b.kv + (int64_t)pg * b.page_stride;
+          src = page + (isv ? kPageRows * Hkv * HD : 0) + (size_t)(kr % kPageRows) * (Hkv * HD) + g * HD + dc * 8;
+        } else {
+          src = seq_base + (size_t)kr * ld + (isv ? vcol : kcol) + dc * 8;
+        }
         lds_u16_t* dst = (isv ? dV : dK) + (isv ? ins - NLI : ins) * KPI * HD;
         load_lds16(src, dst);
       }

@@ -247,6 +247,44 @@ void launch_head(hipStream_t s, int cap_scores, const float* X, DevBatch b, cons
 }
 
 // ---------------------------------------------------------------------------
+// Session KV store: the K and V of each new prefix row of a session sequence
+// go to row rho % kPageRows of its page rho / kPageRows, in the layer's block
+// (an append to the cached prefix KV: "DuoLM: Fast and Effective Personalized
+// Recommendation with Language Models", 未来方向 (3)).  One wave per row,
+// 16 bytes per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_kv_store(const uint16_t* __restrict__ QKV, int ld, DevBatch b, int H,
+                                                  int Hkv, int hd) {
+  const int T = b.hdr->T;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= T) return;
+  int lo = 0, hi = b.hdr->n_seq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (b.seq_row_off[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const SeqDesc sd = b.seqs[lo];
+  const int rho = row - sd.row_off;
+  if (sd.pt < 0 || rho >= sd.L) return;  // not a session sequence, or a branch row
+  const int kvw = Hkv * hd;
+  const int pg = b.pages[sd.pt + rho / kPageRows];
+  uint16_t* dst = b.kv + (int64_t)pg * b.page_stride + (size_t)(rho % kPageRows) * kvw;
+  const uint16_t* src = QKV + (size_t)row * ld + H * hd;  // K then V, kvw values each
+  for (int c = lane; c < kvw / 4; c += 64) {  // 16-byte chunks of K (first half) and V (second half)
+    const bool isv = c >= kvw / 8;
+    const int cc = isv ? c - kvw / 8 : c;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (isv ? kvw : 0) + cc * 8);
+    *reinterpret_cast<uint4*>(dst + (isv ? (size_t)kPageRows * kvw : 0) + cc * 8) = v;
+  }
+}
+
+void launch_kv_store(hipStream_t s, int cap_rows, const uint16_t* QKV, int ld, DevBatch b, int H, int Hkv, int hd) {
+  if (cap_rows <= 0) return;
+  hipLaunchKernelGGL(k_kv_store, dim3((cap_rows + 3) / 4), dim3(256), 0, s, QKV, ld, b, H, Hkv, hd);
+}
+
+// ---------------------------------------------------------------------------
 // Plain 16-byte copy (grid-stride), used to calibrate byte counters.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_copy(uint4* __restrict__ dst, const uint4* __restrict__ src, size_t n) {

@@ -16,6 +16,10 @@ struct DevBatch {
   const WorkItem* bitems;
   const int32_t* head_rows;
   int32_t* err;  // call-wide flag: nonzero after an out-of-range id
+  // session KV pages (null when the call has no session sequences)
+  const int32_t* pages;  // page tables of the call's session sequences
+  uint16_t* kv;          // this layer's K/V block in page 0 of the pool
+  int64_t page_stride;   // elements from one page to the next
 };
 
 // Grids are sized from host upper bounds ("cap" arguments); every kernel reads
@@ -32,6 +36,9 @@ void launch_qk_rope(hipStream_t s, int cap_rows, uint16_t* QKV, int ld, const Ca
 void launch_head(hipStream_t s, int cap_scores, const float* X, DevBatch b, const float* gf,
                  const float* w, float* scores, int d, float eps);
 void launch_copy(hipStream_t s, void* dst, const void* src, size_t nbytes);
+// Store the K and V of the new prefix rows of session sequences into their
+// pages (the layer's block, b.kv).  Rows of other sequences are skipped.
+void launch_kv_store(hipStream_t s, int cap_rows, const uint16_t* QKV, int ld, DevBatch b, int H, int Hkv, int hd);
 
 // GEMM epilogues
 enum { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
