@@ -373,6 +373,57 @@ def bench_export(ranker, cfg, reps):
     return out
 
 
+def bench_session(ranker, cfg, steps):
+    """In-session incremental personalisation ([digest] 未来方向 (3)): 64 users
+    with the headline workload's histories; at every step each user gets one
+    new history item (marker, VID, clip(Poisson(40), 5, 120) feedback ids) and
+    100 candidates are scored.  Incremental: the session appends the item's
+    rows to its cached prefix K/V and scores.  Recompute: the whole prefix is
+    prefilled again with the candidates (one-call MIS).  Both return the same
+    scores bit for bit (checked)."""
+    import synth
+    C, K = 64, 100
+    users = synth.make_requests(3, cfg, n_requests=C, seed=77)
+    marker, _ = synth.template(3, cfg)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(177)))
+    V, N = cfg.vocab, cfg.n_vid
+    ranker.kv_pool_init(C * (600 + (steps + 3) * 130))
+    sess = [ranker.session() for _ in range(C)]
+    prefixes = [u.prefix.copy() for u in users]
+    ranker.step(sess, prefixes)  # the users' histories so far
+    out = {"users": C, "candidates": K, "steps": steps}
+    t_inc, t_full, rows_inc, rows_full = 0.0, 0.0, 0, 0
+    for step in range(steps + 2):  # two untimed warm-up steps (graph capture)
+        new = []
+        for _ in range(C):
+            f = int(np.clip(rng.poisson(40), 5, 120))
+            new.append(np.concatenate([[marker, V + int(rng.integers(0, N))],
+                                       rng.integers(0, V, size=f)]).astype(np.int32))
+        cands = [(V + rng.choice(N, size=K, replace=False)).astype(np.int32) for _ in range(C)]
+        prefixes = [np.concatenate([p, x]) for p, x in zip(prefixes, new)]
+        t0 = time.perf_counter()
+        got = ranker.step(sess, new, cands)
+        t1 = time.perf_counter()
+        want = ranker.score(list(zip(prefixes, cands)))
+        t2 = time.perf_counter()
+        if not np.array_equal(got, want):
+            raise RuntimeError("session scores differ from one-call scores")
+        if step >= 2:
+            t_inc += t1 - t0
+            t_full += t2 - t1
+            rows_inc += sum(len(x) for x in new) + C * K
+            rows_full += sum(len(p) for p in prefixes) + C * K
+    for x in sess:
+        x.close()
+    out["mean_prefix_len_end"] = round(float(np.mean([len(p) for p in prefixes])), 1)
+    out["incremental"] = {"ms_per_step": round(t_inc / steps * 1e3, 3), "scores_per_s": round(C * K * steps / t_inc),
+                          "rows_per_step": round(rows_inc / steps)}
+    out["recompute"] = {"ms_per_step": round(t_full / steps * 1e3, 3), "scores_per_s": round(C * K * steps / t_full),
+                        "rows_per_step": round(rows_full / steps)}
+    out["speedup"] = round(t_full / t_inc, 2)
+    return out
+
+
 def summarize_traffic(out_dir, warmup, steps, pool_size):
     """Turn the four counter passes (FETCH_SIZE and WRITE_SIZE of the gate/up
     GEMM in an eager `--no-graph --open-loop 0 --cpu-baseline-s 0` run with the
@@ -472,13 +523,14 @@ def main():
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
     ap.add_argument("--summarize-traffic", metavar="DIR",
                     help="write profiles/traffic_gemm_gateup.json from the counter runs under DIR (no GPU)")
-    ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export", "packer"],
+    ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export", "packer", "session"],
                     default="headline",
                     help="headline: C=64 x K=100 (the metric); latency: one L=452 x K=100 request per call; "
                          "rating: K=8 at C=8, graph vs eager and ids vs inline vectors; multivec: items of 8 "
                          "vectors, K in {5,20,50,100}, C=1 and C=8; stress: L=4096 x K=512, MIS vs independent; "
                          "export: the offline FP16 export of a 200k-row item table; packer: the host input "
-                         "packer and the host serving path")
+                         "packer and the host serving path; session: incremental history appends against "
+                         "prefix recompute")
     args = ap.parse_args()
 
     if args.summarize_traffic:
@@ -523,6 +575,8 @@ def main():
             res = bench_export(ranker, cfg, reps=20)
         elif args.workload == "packer":
             res = bench_packer(ranker, cfg)
+        elif args.workload == "session":
+            res = bench_session(ranker, cfg, steps=5)
         else:
             res = bench_stress(ranker, cfg, n_req=16, n_ind=32)
         print(json.dumps({"workload": args.workload, **res}), flush=True)
