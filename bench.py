@@ -602,14 +602,17 @@ def main():
     log("warmup")
     for i in range(args.warmup):
         call(batches[i])
-    # time the dominant kernel (gate/up GEMM) and the branch attention live
-    ranker.set_profiling(["gemm_gateup", "attn_branch"])
+    # time the dominant kernel (gate/up GEMM) live; the branch attention is
+    # timed in a pass of its own after the timed region (timing it here would
+    # split the attention launch that otherwise runs prefix and branch tiles
+    # together)
+    ranker.set_profiling(["gemm_gateup"])
     if use_graph:
         # steady state of a serving process: every shape bucket the timed
         # batches fall in has its graph (with its timing events) captured
         for i in range(args.warmup, n_calls):
             call(batches[i])
-        ranker.set_profiling(["gemm_gateup", "attn_branch"])  # reset counters, keep the graphs
+        ranker.set_profiling(["gemm_gateup"])  # reset counters, keep the graphs
     lat = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -623,6 +626,10 @@ def main():
     rows = [int(b[1].sum() + b[2].sum()) for b in batches[args.warmup:]]
     value = n_scores / dt
     gu = ranker.kernel_stats("gemm_gateup")
+    ranker.set_profiling(["attn_branch"])
+    for i in range(args.warmup, min(n_calls, args.warmup + 10)):
+        call(batches[i])
+    torch.cuda.synchronize()
     br = ranker.kernel_stats("attn_branch")
     ranker.set_profiling([])
     if gu.launches == 0 or br.launches == 0:
@@ -659,6 +666,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(gu_ms, 4), "flops_per_launch": gu_flops},
         "roofline_branch_attn": {"kernel": "attn_branch (k_attn, branch tiles)", "bound": "hbm",
+                                 "timed": "10 steps after the timed region, branch tiles launched on their own",
                                  "achieved": round(br_bytes / (br_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                                  "unit": "GB/s", "frac": round(br_bytes / (br_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                  "avg_launch_ms": round(br_ms, 4), "bytes_per_launch": br_bytes},

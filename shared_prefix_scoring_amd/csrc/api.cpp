@@ -61,6 +61,13 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int64_t kDefaultMaxRows = 262144;
 
+// Launch prefix and branch attention tiles together (build with
+// -DDUOLM_MERGED_ATTN=0 for two launches per layer).
+#ifndef DUOLM_MERGED_ATTN
+#define DUOLM_MERGED_ATTN 1
+#endif
+constexpr bool kMergedAttn = DUOLM_MERGED_ATTN != 0;
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Bucket an upper bound: smallest m * 2^e >= x with m in [16, 32], so a
@@ -681,11 +688,20 @@ void enqueue_forward(Enq& q, const Caps& c) {
     });
     if (q.stop(l, DUOLM_STAGE_QK_ROPE)) return;
     if (c.session) launch_kv_store(s, c.T, R->QKV, nq, bl, H, Hk, hd);
-    q.run(DUOLM_K_ATTN_PREFIX,
-          [&] { launch_attn(s, false, hd, c.pitems, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
-    if (c.bitems > 0)
-      q.run(DUOLM_K_ATTN_BRANCH,
-            [&] { launch_attn(s, true, hd, c.bitems, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
+    // prefix and branch tiles in one launch, side by side on the chip; apart
+    // when either kind is being timed
+    const bool split = !kMergedAttn || ((R->prof_mask >> DUOLM_K_ATTN_PREFIX) & 1u) ||
+                       ((R->prof_mask >> DUOLM_K_ATTN_BRANCH) & 1u);
+    if (split) {
+      q.run(DUOLM_K_ATTN_PREFIX,
+            [&] { launch_attn(s, hd, c.pitems, 0, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
+      if (c.bitems > 0)
+        q.run(DUOLM_K_ATTN_BRANCH,
+              [&] { launch_attn(s, hd, 0, c.bitems, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
+    } else {
+      q.run(DUOLM_K_ATTN_PREFIX,
+            [&] { launch_attn(s, hd, c.pitems, c.bitems, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
+    }
     if (q.stop(l, DUOLM_STAGE_ATTN)) return;
     q.run(DUOLM_K_GEMM_O, [&] { launch_gemm(s, EPI_RESID, c.T, R->Ob, H * hd, W.wo, H * hd, R->X, d, dT, d, H * hd); });
     if (q.stop(l, DUOLM_STAGE_ATTN_RESID)) return;

@@ -55,8 +55,10 @@ __device__ __forceinline__ v4i16_t lds_read_tr16(const lds_u16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
 }
 
-// One instantiation serves both row kinds (`branch` is a runtime flag), so a
-// candidate row and a causal row run the very same instruction sequence.
+// One instantiation serves both row kinds, so a candidate row and a causal
+// row run the very same instruction sequence.  A launch may carry both kinds:
+// blocks [0, pcap) take prefix tiles, the rest branch tiles, so the two run
+// side by side on the chip (both are latency-bound, one workgroup per CU).
 // V chunk swizzle: the four consecutive keys of a transpose read land in four
 // different 16-chunk quarters of the bank space.
 template <int CPR>
@@ -77,8 +79,9 @@ constexpr float kLazyTau = 8.0f;
 template <int HD, int NW, int BKV>
 __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ QKV, int ld,
                                                  uint16_t* __restrict__ O, int ldo, DevBatch b, int H,
-                                                 int Hkv, float scale_log2, int branch) {
-  const bool BRANCH = branch != 0;
+                                                 int Hkv, float scale_log2, int pcap) {
+  const bool BRANCH = (int)blockIdx.x >= pcap;
+  const int idx = BRANCH ? (int)blockIdx.x - pcap : (int)blockIdx.x;
   constexpr int NKS = HD / 16;         // k-steps of the QK^T product
   constexpr int NDB = HD / 32;         // 32-dim blocks of the output
   constexpr int CPR = HD / 8;          // 16-byte chunks per key row / per query column
@@ -106,9 +109,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   // the item and the item count load together (the grid never exceeds the
   // item buffer, so the read is in bounds even for surplus blocks; testing
   // one of its fields in the exit condition keeps its load above the branch)
-  const WorkItem item = (BRANCH ? b.bitems : b.pitems)[blockIdx.x];
+  const WorkItem item = (BRANCH ? b.bitems : b.pitems)[idx];
   const int n_items = BRANCH ? b.hdr->n_bitems : b.hdr->n_pitems;
-  if ((int)blockIdx.x >= n_items || item.L < 1) return;
+  if (idx >= n_items || item.L < 1) return;
   struct {
     int row_off, L, K;
   } const sd = {item.row_off, item.L, item.K};
@@ -456,11 +459,11 @@ constexpr int NW = ATTN_NW;    // query columns per workgroup = 32 NW
 constexpr int BKV = ATTN_BKV;  // keys per streamed tile
 
 template <int HD>
-void launch_hd(hipStream_t s, bool branch, int cap_items, const uint16_t* QKV, int ld, uint16_t* O, int ldo,
+void launch_hd(hipStream_t s, int cap_p, int cap_b, const uint16_t* QKV, int ld, uint16_t* O, int ldo,
                DevBatch b, int H, int Hkv, float scale_log2) {
-  const dim3 grid(cap_items, Hkv);
+  const dim3 grid(cap_p + cap_b, Hkv);
   hipLaunchKernelGGL((k_attn<HD, NW, BKV>), grid, dim3(NW * 64), 0, s, QKV, ld, O, ldo, b, H, Hkv, scale_log2,
-                     branch ? 1 : 0);
+                     cap_p);
 }
 
 }  // namespace
@@ -469,12 +472,12 @@ int attn_rows_per_item(bool, int group) { return NW * 32 / group; }
 
 bool attn_supported(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 
-void launch_attn(hipStream_t s, bool branch, int hd, int cap_items, const uint16_t* QKV, int ld, uint16_t* O,
-                 int ldo, DevBatch b, int H, int Hkv, float scale_log2) {
-  if (cap_items <= 0) return;
-  if (hd == 128) launch_hd<128>(s, branch, cap_items, QKV, ld, O, ldo, b, H, Hkv, scale_log2);
-  else if (hd == 64) launch_hd<64>(s, branch, cap_items, QKV, ld, O, ldo, b, H, Hkv, scale_log2);
-  else launch_hd<32>(s, branch, cap_items, QKV, ld, O, ldo, b, H, Hkv, scale_log2);
+void launch_attn(hipStream_t s, int hd, int cap_p, int cap_b, const uint16_t* QKV, int ld, uint16_t* O, int ldo,
+                 DevBatch b, int H, int Hkv, float scale_log2) {
+  if (cap_p + cap_b <= 0) return;
+  if (hd == 128) launch_hd<128>(s, cap_p, cap_b, QKV, ld, O, ldo, b, H, Hkv, scale_log2);
+  else if (hd == 64) launch_hd<64>(s, cap_p, cap_b, QKV, ld, O, ldo, b, H, Hkv, scale_log2);
+  else launch_hd<32>(s, cap_p, cap_b, QKV, ld, O, ldo, b, H, Hkv, scale_log2);
 }
 
 }  // namespace duolm

@@ -50,8 +50,9 @@ bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, 
 // Attention over one launch's work items.  Returns rows covered per item.
 int attn_rows_per_item(bool branch, int group);
 bool attn_supported(int head_dim);
-void launch_attn(hipStream_t s, bool branch, int hd, int cap_items, const uint16_t* QKV, int ld,
-                 uint16_t* O, int ldo, DevBatch b, int H, int Hkv, float scale_log2);
+// cap_p prefix-tile blocks and cap_b branch-tile blocks in one launch (either may be 0).
+void launch_attn(hipStream_t s, int hd, int cap_p, int cap_b, const uint16_t* QKV, int ld, uint16_t* O, int ldo,
+                 DevBatch b, int H, int Hkv, float scale_log2);
 
 // Offline export of encoder outputs a[n_rows, d] (16-byte aligned rows of
 // dtype EXPORT_*) into FP16 rows z = scale * a / sqrt(mean(a^2) + eps).
