@@ -118,17 +118,14 @@ struct Timed {
   hipEvent_t a, b;
 };
 
-// A captured forward.  Without profiling it is one graph.  With profiling it
-// is split into segments so that every timed kernel is a graph of its own:
-// HIP events cannot time nodes inside a graph, but events recorded on the
-// stream between segment launches can.  cls is the kernel class a segment
-// times, or -1.
-struct GraphSeg {
-  hipGraphExec_t exec;
-  int cls;
-};
+// A captured forward: one executable graph.  With profiling, every timed
+// kernel is bracketed by event-record nodes added to the graph while it is
+// captured (an event recorded on a capturing stream is not captured, but an
+// explicit event-record node is, and times the nodes between its pair).  The
+// events belong to the graph; each replay overwrites them.
 struct GraphEntry {
-  std::vector<GraphSeg> segs;
+  hipGraphExec_t exec = nullptr;
+  std::vector<Timed> timed;
 };
 
 }  // namespace
@@ -396,10 +393,18 @@ int create_from_blob(const void* blob, uint64_t nbytes, int dev, duolm_ranker** 
 // ---------------------------------------------------------------------------
 // capacities
 // ---------------------------------------------------------------------------
+void free_graph(GraphEntry& ge) {
+  if (ge.exec) (void)hipGraphExecDestroy(ge.exec);
+  ge.exec = nullptr;
+  for (const Timed& t : ge.timed) {
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  ge.timed.clear();
+}
+
 void drop_graphs(duolm_ranker* R) {
-  for (auto& kv : R->graphs)
-    for (auto& sg : kv.second.segs)
-      if (sg.exec) (void)hipGraphExecDestroy(sg.exec);
+  for (auto& kv : R->graphs) free_graph(kv.second);
   R->graphs.clear();
 }
 
@@ -621,29 +626,40 @@ struct Enq {
   bool stopped = false;
   hipError_t cap_err = hipSuccess;
 
-  void end_segment(int cls) {
-    hipGraph_t g = nullptr;
-    hipError_t e = hipStreamEndCapture(s, &g);
-    hipGraphExec_t ex = nullptr;
-    if (e == hipSuccess) e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-    if (g) (void)hipGraphDestroy(g);
-    if (e == hipSuccess) capture->segs.push_back({ex, cls});
-    else if (cap_err == hipSuccess) cap_err = e;
-  }
-  void begin_segment() {
-    const hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  void note(hipError_t e) {
     if (e != hipSuccess && cap_err == hipSuccess) cap_err = e;
+  }
+  // append an event-record node after everything captured so far
+  void record_node(hipEvent_t ev) {
+    hipStreamCaptureStatus st;
+    unsigned long long id = 0;
+    hipGraph_t g = nullptr;
+    const hipGraphNode_t* deps = nullptr;
+    size_t nd = 0;
+    hipError_t e = hipStreamGetCaptureInfo_v2(s, &st, &id, &g, &deps, &nd);
+    hipGraphNode_t n = nullptr;
+    if (e == hipSuccess) e = hipGraphAddEventRecordNode(&n, g, deps, nd, ev);
+    if (e == hipSuccess) e = hipStreamUpdateCaptureDependencies(s, &n, 1, hipStreamSetCaptureDependencies);
+    note(e);
   }
 
   template <typename F>
   void run(int cls, F&& f) {
     const bool want = R->prof_mask >> cls & 1u;
-    if (capture && want) {  // the timed kernel becomes a segment of its own
-      end_segment(-1);
-      begin_segment();
+    if (capture && want) {  // bracket the kernel with event-record nodes
+      hipEvent_t a = nullptr, b = nullptr;
+      note(hipEventCreate(&a));
+      note(hipEventCreate(&b));
+      if (cap_err != hipSuccess) {
+        if (a) (void)hipEventDestroy(a);
+        if (b) (void)hipEventDestroy(b);
+        f();
+        return;
+      }
+      capture->timed.push_back({cls, a, b});
+      record_node(a);
       f();
-      end_segment(cls);
-      begin_segment();
+      record_node(b);
       return;
     }
     if (!capture && timed && want) {
@@ -785,28 +801,22 @@ int run_launch(duolm_ranker* R, const Plan& P, hipStream_t s, bool use_graph, st
   if (it == R->graphs.end()) {
     GraphEntry ge;
     Enq q{R, s, nullptr, &ge};
-    q.begin_segment();
-    enqueue_forward(q, c);
-    q.end_segment(-1);
+    q.note(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    if (q.cap_err == hipSuccess) enqueue_forward(q, c);
+    hipGraph_t g = nullptr;
+    q.note(hipStreamEndCapture(s, &g));
+    if (q.cap_err == hipSuccess) q.note(hipGraphInstantiate(&ge.exec, g, nullptr, nullptr, 0));
+    if (g) (void)hipGraphDestroy(g);
     if (q.cap_err != hipSuccess) {
-      for (auto& sg : ge.segs) (void)hipGraphExecDestroy(sg.exec);
+      free_graph(ge);
       return fail(DUOLM_EHIP, "graph capture: %s", hipGetErrorString(q.cap_err));
     }
     it = R->graphs.emplace(c, std::move(ge)).first;
   }
-  for (const GraphSeg& sg : it->second.segs) {
-    if (sg.cls >= 0 && timed) {
-      hipEvent_t a = pool_event(R), b = pool_event(R);
-      if (a && b) {
-        HIP_TRY(hipEventRecord(a, s));
-        HIP_TRY(hipGraphLaunch(sg.exec, s));
-        HIP_TRY(hipEventRecord(b, s));
-        timed->push_back({sg.cls, a, b});
-        continue;
-      }
-    }
-    HIP_TRY(hipGraphLaunch(sg.exec, s));
-  }
+  HIP_TRY(hipGraphLaunch(it->second.exec, s));
+  // the graph's events hold this replay's times until its next replay: the
+  // caller reads them before launching the same graph again
+  if (timed) timed->insert(timed->end(), it->second.timed.begin(), it->second.timed.end());
   return DUOLM_OK;
 }
 
@@ -950,24 +960,26 @@ int run_plans(duolm_ranker* R, const std::vector<Plan>& plans, const int32_t* id
   HIP_TRY(hipMemcpyAsync(R->d_err, R->h_err, 4, hipMemcpyHostToDevice, s));
   R->ev_used = 0;
   std::vector<Timed> timed_ev;
-  std::vector<std::pair<size_t, Plan const*>> plan_marks;  // timed_ev index where each plan starts
   for (const Plan& P : plans) {
-    plan_marks.push_back({timed_ev.size(), &P});
+    timed_ev.clear();
     if ((rc = run_launch(R, P, s, use_graph, &timed_ev))) {
       (void)hipStreamSynchronize(s);
       return rc;
     }
+    if (R->prof_mask && plans.size() > 1) {  // read this launch's times before a replay can overwrite them
+      HIP_TRY(hipStreamSynchronize(s));
+      double fl[DUOLM_K_COUNT], by[DUOLM_K_COUNT];
+      launch_work(R, P, fl, by);
+      add_stats(R, timed_ev, fl, by);
+      timed_ev.clear();
+    }
   }
   HIP_TRY(hipMemcpyAsync(R->h_err, R->d_err, 4, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
-  if (R->prof_mask) {
+  if (R->prof_mask && plans.size() == 1) {
     double fl[DUOLM_K_COUNT], by[DUOLM_K_COUNT];
-    for (size_t i = 0; i < plan_marks.size(); ++i) {
-      const size_t end = i + 1 < plan_marks.size() ? plan_marks[i + 1].first : timed_ev.size();
-      launch_work(R, *plan_marks[i].second, fl, by);
-      std::vector<Timed> part(timed_ev.begin() + plan_marks[i].first, timed_ev.begin() + end);
-      add_stats(R, part, fl, by);
-    }
+    launch_work(R, plans[0], fl, by);
+    add_stats(R, timed_ev, fl, by);
   }
   if (*R->h_err) return fail(DUOLM_ERANGE, "an id in the device batch is outside [0, V + N)");
   if (total_scores > 0) {
