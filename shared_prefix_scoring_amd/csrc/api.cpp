@@ -68,6 +68,13 @@ constexpr int64_t kDefaultMaxRows = 262144;
 #endif
 constexpr bool kMergedAttn = DUOLM_MERGED_ATTN != 0;
 
+// Run the last layer past its QKV projection over the branch rows only
+// (build with -DDUOLM_BRANCH_ONLY_TAIL=0 to compute every row there).
+#ifndef DUOLM_BRANCH_ONLY_TAIL
+#define DUOLM_BRANCH_ONLY_TAIL 1
+#endif
+constexpr bool kBranchOnlyTail = DUOLM_BRANCH_ONLY_TAIL != 0;
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Bucket an upper bound: smallest m * 2^e >= x with m in [16, 32], so a
@@ -95,6 +102,8 @@ struct LayerW {
 // One forward launch.
 struct Plan {
   int T = 0;
+  int TB = 0, TP = 0;  // rows of the branch region (packed first) and of the prefix region
+  std::vector<int32_t> bstart, pstart;  // per sequence: first branch row, first prefix row (region-relative)
   std::vector<int32_t> seq_row_off;
   std::vector<SeqDesc> seqs;
   std::vector<WorkItem> pitems, bitems;
@@ -106,16 +115,17 @@ struct Plan {
 };
 
 struct Caps {
-  int T, seq, pitems, bitems, scores, pages, session;
+  int T, seq, pitems, bitems, scores, pages, session, brows;
   bool operator<(const Caps& o) const {
-    return std::tie(T, seq, pitems, bitems, scores, pages, session) <
-           std::tie(o.T, o.seq, o.pitems, o.bitems, o.scores, o.pages, o.session);
+    return std::tie(T, seq, pitems, bitems, scores, pages, session, brows) <
+           std::tie(o.T, o.seq, o.pitems, o.bitems, o.scores, o.pages, o.session, o.brows);
   }
 };
 
 struct Timed {
   int cls;
   hipEvent_t a, b;
+  bool brows;  // the launch ran over the branch rows only (the last layer)
 };
 
 // A captured forward: one executable graph.  With profiling, every timed
@@ -446,7 +456,7 @@ int ensure_meta(duolm_ranker* R, int n_seq, int n_pi, int n_bi, int n_hs, int n_
   R->cap_hs = grow(n_hs, R->cap_hs);
   R->cap_pt = grow(n_pt, R->cap_pt);
   size_t off = align_up(sizeof(CallHeader), 256);
-  R->off_sro = off; off = align_up(off + (size_t)(R->cap_seq + 1) * 4, 256);
+  R->off_sro = off; off = align_up(off + (size_t)(2 * R->cap_seq + 1) * 4, 256);
   R->off_seq = off; off = align_up(off + (size_t)R->cap_seq * sizeof(SeqDesc), 256);
   R->off_pi = off; off = align_up(off + (size_t)R->cap_pi * sizeof(WorkItem), 256);
   R->off_bi = off; off = align_up(off + (size_t)R->cap_bi * sizeof(WorkItem), 256);
@@ -503,11 +513,16 @@ DevBatch dev_batch(duolm_ranker* R) {
 // A sequence: L causal rows, then K candidate branches of M rows each.
 // Branch attention tiles hold whole branches (a branch row's in-branch keys
 // are rows of its own tile); the score head reads each branch's last row.
+// Branch rows go to the branch region, prefix rows to the prefix region that
+// follows it; prefix-side offsets are region-relative until plan_close adds
+// the branch region's size.
 void plan_add_seq(duolm_ranker* R, Plan& P, int L, int K, int M, int id_off, int id_len, int cand_id_off) {
   const int G = R->dims.n_heads / R->dims.n_kv_heads;
   const int s = (int)P.seqs.size();
+  const int KM = K * M;
   SeqDesc sd{};
-  sd.row_off = P.T;
+  sd.row_off = P.TP;
+  sd.boff = P.TB - L;
   sd.L = L;
   sd.K = K;
   sd.id_off = id_off;
@@ -517,28 +532,31 @@ void plan_add_seq(duolm_ranker* R, Plan& P, int L, int K, int M, int id_off, int
   sd.pt = -1;
   P.seqs.push_back(sd);
   P.cached.push_back(0);
-  P.seq_row_off.push_back(P.T);
+  P.pstart.push_back(P.TP);
+  P.bstart.push_back(P.TB);
   const int rp = attn_rows_per_item(false, G);
   const int rb = attn_rows_per_item(true, G) / M * M;  // whole branches per tile
-  const int KM = K * M;
-  for (int r0 = 0; r0 < L; r0 += rp) P.pitems.push_back({s, r0, P.T, L, KM, M, -1, 0});
-  for (int c0 = 0; c0 < KM; c0 += rb) P.bitems.push_back({s, c0, P.T, L, KM, M, -1, 0});
-  for (int j = 0; j < K; ++j) P.head_rows.push_back(P.T + L + j * M + M - 1);
+  for (int r0 = 0; r0 < L; r0 += rp) P.pitems.push_back({s, r0, sd.row_off, L, KM, M, -1, sd.row_off});
+  for (int c0 = 0; c0 < KM; c0 += rb) P.bitems.push_back({s, c0, sd.boff, L, KM, M, -1, sd.row_off});
+  for (int j = 0; j < K; ++j) P.head_rows.push_back(P.TB + j * M + M - 1);
+  P.TP += L;
+  P.TB += KM;
   P.T += L + KM;
 }
 
 // A session sequence: prefix rows [0, Lc) were computed by earlier calls (their
 // K and V are in the session's pages), rows [Lc, L) are new, then K branches.
 // Only the new rows and the branches are packed; row_off and id_off are
-// virtual (row Lc sits at the packed position P.T).  ids: the new prefix ids
-// at new_id_off, the candidates' at cand_id_off.
+// virtual (row Lc sits at the prefix region's next row).  ids: the new prefix
+// ids at new_id_off, the candidates' at cand_id_off.
 void plan_add_session(duolm_ranker* R, Plan& P, int Lc, int L, int K, int M, int new_id_off, int cand_id_off,
                       const std::vector<int32_t>& pages) {
   const int G = R->dims.n_heads / R->dims.n_kv_heads;
   const int s = (int)P.seqs.size();
-  const int voff = P.T - Lc;
+  const int KM = K * M;
   SeqDesc sd{};
-  sd.row_off = voff;
+  sd.row_off = P.TP - Lc;
+  sd.boff = P.TB - L;
   sd.L = L;
   sd.K = K;
   sd.id_off = new_id_off - Lc;
@@ -549,20 +567,32 @@ void plan_add_session(duolm_ranker* R, Plan& P, int Lc, int L, int K, int M, int
   P.pages.insert(P.pages.end(), pages.begin(), pages.begin() + (L + kPageRows - 1) / kPageRows);
   P.seqs.push_back(sd);
   P.cached.push_back(Lc);
-  P.seq_row_off.push_back(P.T);
+  P.pstart.push_back(P.TP);
+  P.bstart.push_back(P.TB);
   const int rp = attn_rows_per_item(false, G);
   const int rb = attn_rows_per_item(true, G) / M * M;
-  const int KM = K * M;
-  for (int r0 = Lc; r0 < L; r0 += rp) P.pitems.push_back({s, r0, voff, L, KM, M, sd.pt, 0});
-  for (int c0 = 0; c0 < KM; c0 += rb) P.bitems.push_back({s, c0, voff, L, KM, M, sd.pt, 0});
-  for (int j = 0; j < K; ++j) P.head_rows.push_back(P.T + (L - Lc) + j * M + M - 1);
+  for (int r0 = Lc; r0 < L; r0 += rp) P.pitems.push_back({s, r0, sd.row_off, L, KM, M, sd.pt, sd.row_off});
+  for (int c0 = 0; c0 < KM; c0 += rb) P.bitems.push_back({s, c0, sd.boff, L, KM, M, sd.pt, sd.row_off});
+  for (int j = 0; j < K; ++j) P.head_rows.push_back(P.TB + j * M + M - 1);
+  P.TP += L - Lc;
+  P.TB += KM;
   P.T += (L - Lc) + KM;
   P.session = true;
 }
 
-// Close a launch: attention tiles go longest first (their key count is the
-// work), so the grid's tail is made of short tiles.
+// Close a launch: place the prefix region after the branch region, build the
+// row-to-segment table, and order the attention tiles longest first (their
+// key count is the work), so the grid's tail is made of short tiles.
 void plan_close(duolm_ranker* R, Plan& P) {
+  const int TB = P.TB;
+  for (SeqDesc& sd : P.seqs) sd.row_off += TB;
+  for (WorkItem& w : P.pitems) {
+    w.row_off += TB;
+    w.koff += TB;
+  }
+  for (WorkItem& w : P.bitems) w.koff += TB;
+  P.seq_row_off.assign(P.bstart.begin(), P.bstart.end());
+  for (int32_t p : P.pstart) P.seq_row_off.push_back(TB + p);
   P.seq_row_off.push_back(P.T);
   const int G = R->dims.n_heads / R->dims.n_kv_heads;
   const int rp = attn_rows_per_item(false, G);
@@ -574,9 +604,12 @@ void plan_close(duolm_ranker* R, Plan& P) {
 }
 
 // Algorithmic FLOPs and bytes of one launch per kernel class.
-void launch_work(const duolm_ranker* R, const Plan& P, double fl[DUOLM_K_COUNT], double by[DUOLM_K_COUNT]) {
+// rows: the rows a row-wise launch covers (all T, or the branch rows of the
+// last layer).
+void launch_work(const duolm_ranker* R, const Plan& P, double fl[DUOLM_K_COUNT], double by[DUOLM_K_COUNT],
+                 double rows) {
   const auto& D = R->dims;
-  const double T = P.T, d = D.d_model, H = D.n_heads, Hk = D.n_kv_heads, hd = D.head_dim, F = D.d_ffn;
+  const double T = rows, d = D.d_model, H = D.n_heads, Hk = D.n_kv_heads, hd = D.head_dim, F = D.d_ffn;
   const double nq = R->nqkv;
   for (int i = 0; i < DUOLM_K_COUNT; ++i) fl[i] = by[i] = 0;
   by[DUOLM_K_EMBED] = T * (d * 2 + d * 4 + 8);
@@ -624,6 +657,7 @@ struct Enq {
   GraphEntry* capture;        // graph capture in progress (null: eager)
   int stop_layer = -1, stop_stage = -1;
   bool stopped = false;
+  bool brows = false;  // the launches being enqueued cover the branch rows only
   hipError_t cap_err = hipSuccess;
 
   void note(hipError_t e) {
@@ -656,7 +690,7 @@ struct Enq {
         f();
         return;
       }
-      capture->timed.push_back({cls, a, b});
+      capture->timed.push_back({cls, a, b, brows});
       record_node(a);
       f();
       record_node(b);
@@ -668,7 +702,7 @@ struct Enq {
         (void)hipEventRecord(a, s);
         f();
         (void)hipEventRecord(b, s);
-        timed->push_back({cls, a, b});
+        timed->push_back({cls, a, b, brows});
         return;
       }
     }
@@ -689,13 +723,20 @@ void enqueue_forward(Enq& q, const Caps& c) {
   hipStream_t s = q.s;
   DevBatch b = dev_batch(R);
   const int32_t* dT = &b.hdr->T;
+  const int32_t* dB = &b.hdr->n_brows;
   q.run(DUOLM_K_EMBED, [&] { launch_embed(s, c.T, R->d_ids, b, R->embed, R->vid, R->d_inline, D.vocab, R->n_vid, d, R->X, R->pos); });
   if (q.stop(0, DUOLM_STAGE_EMBED)) return;
   for (int l = 0; l < D.n_layers; ++l) {
     const LayerW& W = R->layers[l];
     DevBatch bl = b;  // this layer's block of the session KV pages
     if (R->kv_pool) bl.kv = R->kv_pool + (size_t)l * 2 * kPageRows * Hk * hd;
-    q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, c.T, R->X, W.attn_norm, R->Xn, b.hdr, d, eps); });
+    // The last layer's prefix rows feed nothing but their K and V (read by the
+    // branch tiles): after its QKV projection it runs over the branch rows
+    // [0, n_brows) only -- no prefix attention, O projection, MLP.  A debug
+    // stop reads whole layers, so it keeps every row.
+    const bool tail = kBranchOnlyTail && l == D.n_layers - 1 && q.stop_layer < 0;
+    q.brows = false;
+    q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, c.T, R->X, W.attn_norm, R->Xn, dT, d, eps); });
     if (q.stop(l, DUOLM_STAGE_ATTN_NORM)) return;
     q.run(DUOLM_K_GEMM_QKV, [&] { launch_gemm(s, EPI_BF16, c.T, R->Xn, d, W.wqkv, d, R->QKV, nq, dT, nq, d); });
     if (q.stop(l, DUOLM_STAGE_QKV)) return;
@@ -708,7 +749,11 @@ void enqueue_forward(Enq& q, const Caps& c) {
     // when either kind is being timed
     const bool split = !kMergedAttn || ((R->prof_mask >> DUOLM_K_ATTN_PREFIX) & 1u) ||
                        ((R->prof_mask >> DUOLM_K_ATTN_BRANCH) & 1u);
-    if (split) {
+    if (tail) {
+      if (c.bitems > 0)
+        q.run(DUOLM_K_ATTN_BRANCH,
+              [&] { launch_attn(s, hd, 0, c.bitems, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
+    } else if (split) {
       q.run(DUOLM_K_ATTN_PREFIX,
             [&] { launch_attn(s, hd, c.pitems, 0, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
       if (c.bitems > 0)
@@ -719,13 +764,17 @@ void enqueue_forward(Enq& q, const Caps& c) {
             [&] { launch_attn(s, hd, c.pitems, c.bitems, R->QKV, nq, R->Ob, H * hd, bl, H, Hk, scale_log2); });
     }
     if (q.stop(l, DUOLM_STAGE_ATTN)) return;
-    q.run(DUOLM_K_GEMM_O, [&] { launch_gemm(s, EPI_RESID, c.T, R->Ob, H * hd, W.wo, H * hd, R->X, d, dT, d, H * hd); });
+    const int cr = tail ? c.brows : c.T;  // rows (cap) of the rest of the layer
+    const int32_t* dR = tail ? dB : dT;
+    q.brows = tail;
+    q.run(DUOLM_K_GEMM_O, [&] { launch_gemm(s, EPI_RESID, cr, R->Ob, H * hd, W.wo, H * hd, R->X, d, dR, d, H * hd); });
     if (q.stop(l, DUOLM_STAGE_ATTN_RESID)) return;
-    q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, c.T, R->X, W.mlp_norm, R->Xn, b.hdr, d, eps); });
+    q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, cr, R->X, W.mlp_norm, R->Xn, dR, d, eps); });
     if (q.stop(l, DUOLM_STAGE_MLP_NORM)) return;
-    q.run(DUOLM_K_GEMM_GATEUP, [&] { launch_gemm(s, EPI_SWIGLU, c.T, R->Xn, d, W.wgu, d, R->Hb, F, dT, 2 * F, d); });
+    q.run(DUOLM_K_GEMM_GATEUP, [&] { launch_gemm(s, EPI_SWIGLU, cr, R->Xn, d, W.wgu, d, R->Hb, F, dR, 2 * F, d); });
     if (q.stop(l, DUOLM_STAGE_SWIGLU)) return;
-    q.run(DUOLM_K_GEMM_DOWN, [&] { launch_gemm(s, EPI_RESID, c.T, R->Hb, F, W.wdown, F, R->X, d, dT, d, F); });
+    q.run(DUOLM_K_GEMM_DOWN, [&] { launch_gemm(s, EPI_RESID, cr, R->Hb, F, W.wdown, F, R->X, d, dR, d, F); });
+    q.brows = false;
     if (q.stop(l, DUOLM_STAGE_LAYER_OUT)) return;
   }
   if (q.stop_layer >= 0) return;
@@ -746,6 +795,7 @@ int upload_plan(duolm_ranker* R, const Plan& P, hipStream_t s) {
   hdr.n_scores = (int)P.head_rows.size();
   hdr.score_off = P.score_off;
   hdr.n_inline = R->call_n_inline;
+  hdr.n_brows = P.TB;
   memcpy(h, &hdr, sizeof(hdr));
   memcpy(h + R->off_sro, P.seq_row_off.data(), P.seq_row_off.size() * 4);
   memcpy(h + R->off_seq, P.seqs.data(), P.seqs.size() * sizeof(SeqDesc));
@@ -770,15 +820,18 @@ int upload_plan(duolm_ranker* R, const Plan& P, hipStream_t s) {
   return DUOLM_OK;
 }
 
-void add_stats(duolm_ranker* R, const std::vector<Timed>& timed, const double fl[], const double by[]) {
+void add_stats(duolm_ranker* R, const Plan& P, const std::vector<Timed>& timed) {
+  double fl[DUOLM_K_COUNT], by[DUOLM_K_COUNT], flb[DUOLM_K_COUNT], byb[DUOLM_K_COUNT];
+  launch_work(R, P, fl, by, P.T);
+  launch_work(R, P, flb, byb, P.TB);
   for (const Timed& t : timed) {
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, t.a, t.b) != hipSuccess) continue;
     duolm_kernel_stats& st = R->stats[t.cls];
     st.launches += 1;
     st.total_ms += ms;
-    st.flops += fl[t.cls];
-    st.bytes += by[t.cls];
+    st.flops += (t.brows ? flb : fl)[t.cls];
+    st.bytes += (t.brows ? byb : by)[t.cls];
   }
 }
 
@@ -788,7 +841,7 @@ int run_launch(duolm_ranker* R, const Plan& P, hipStream_t s, bool use_graph, st
   if (rc) return rc;
   if (!use_graph) {
     Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(),
-           (int)P.pages.size(), P.session ? 1 : 0};
+           (int)P.pages.size(), P.session ? 1 : 0, P.TB};
     Enq q{R, s, R->prof_mask ? timed : nullptr, nullptr};
     enqueue_forward(q, c);
     HIP_TRY(hipGetLastError());
@@ -796,7 +849,8 @@ int run_launch(duolm_ranker* R, const Plan& P, hipStream_t s, bool use_graph, st
   }
   Caps c{std::min(bucket(P.T), R->cap_T), std::min(bucket((int)P.seqs.size()), R->cap_seq),
          std::min(bucket((int)P.pitems.size()), R->cap_pi), std::min(bucket((int)P.bitems.size()), R->cap_bi),
-         std::min(bucket((int)P.head_rows.size()), R->cap_hs), 0, P.session ? 1 : 0};
+         std::min(bucket((int)P.head_rows.size()), R->cap_hs), 0, P.session ? 1 : 0,
+         std::min(bucket(P.TB), R->cap_T)};
   auto it = R->graphs.find(c);
   if (it == R->graphs.end()) {
     GraphEntry ge;
@@ -968,19 +1022,13 @@ int run_plans(duolm_ranker* R, const std::vector<Plan>& plans, const int32_t* id
     }
     if (R->prof_mask && plans.size() > 1) {  // read this launch's times before a replay can overwrite them
       HIP_TRY(hipStreamSynchronize(s));
-      double fl[DUOLM_K_COUNT], by[DUOLM_K_COUNT];
-      launch_work(R, P, fl, by);
-      add_stats(R, timed_ev, fl, by);
+      add_stats(R, P, timed_ev);
       timed_ev.clear();
     }
   }
   HIP_TRY(hipMemcpyAsync(R->h_err, R->d_err, 4, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
-  if (R->prof_mask && plans.size() == 1) {
-    double fl[DUOLM_K_COUNT], by[DUOLM_K_COUNT];
-    launch_work(R, plans[0], fl, by);
-    add_stats(R, timed_ev, fl, by);
-  }
+  if (R->prof_mask && plans.size() == 1) add_stats(R, plans[0], timed_ev);
   if (*R->h_err) return fail(DUOLM_ERANGE, "an id in the device batch is outside [0, V + N)");
   if (total_scores > 0) {
     HIP_TRY(hipMemcpyAsync(out_dev ? (void*)out : (void*)R->h_stage, R->d_out, (size_t)total_scores * 4,
@@ -1605,7 +1653,7 @@ int duolm_debug_forward(duolm_ranker* R, const duolm_request* reqs, int32_t n_re
   *R->h_err = 0;
   HIP_TRY(hipMemcpyAsync(R->d_err, R->h_err, 4, hipMemcpyHostToDevice, s));
   if ((rc = upload_plan(R, P, s))) return rc;
-  Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(), 0, 0};
+  Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(), 0, 0, P.TB};
   Enq q{R, s, nullptr, nullptr};
   q.stop_layer = layer == D.n_layers ? D.n_layers - 1 : layer;
   q.stop_stage = buf_stage;
@@ -1619,8 +1667,20 @@ int duolm_debug_forward(duolm_ranker* R, const duolm_request* reqs, int32_t n_re
     case DUOLM_STAGE_SWIGLU: src = R->Hb; break;
     default: src = R->X;
   }
-  HIP_TRY(hipMemcpyAsync(host_out, src, nbytes, hipMemcpyDeviceToHost, s));
+  // rows come back in request order -- each sequence's prefix rows, then its
+  // branch rows -- not in the packed order (branch region first)
+  std::vector<char> packed((size_t)nbytes);
+  HIP_TRY(hipMemcpyAsync(packed.data(), src, nbytes, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
+  char* o = (char*)host_out;
+  for (const SeqDesc& sd : P.seqs) {
+    const int rows = sd.L + sd.K * sd.M;
+    for (int rho = 0; rho < rows; ++rho) {
+      const int prow = (rho < sd.L ? sd.row_off : sd.boff) + rho;
+      memcpy(o, packed.data() + (size_t)prow * row_bytes, row_bytes);
+      o += row_bytes;
+    }
+  }
   return DUOLM_OK;
 }
 

@@ -167,7 +167,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   const bool wave_active = __any(qvalid);
   const int kcol = H * HD + g * HD;
   const int vcol = H * HD + Hkv * HD + g * HD;
-  const uint16_t* seq_base = QKV + (size_t)sd.row_off * ld;
+  // packed rows: query row i of the item (and its own K/V) at qrow0 + i, prefix
+  // key k at koff + k (offsets are virtual, so only these sums are addresses)
+  const int qrow0 = sd.row_off + item_row0;
   lds_u16_t* const ldsQ = (lds_u16_t*)(lds_void_t*)Qs;
   // stage ST's K and V tiles
   auto kt = [&](auto st) -> uint16_t* { if constexpr (decltype(st)::value == 0) return sK0; else return sK1; };
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     const int col = c / CPR, slot = c % CPR;
     const int lr = min(col / G, item_nrows - 1);
     const uint16_t* src =
-        seq_base + (size_t)(item_row0 + lr) * ld + (g * G + col % G) * HD + ((slot ^ cswz(col)) << 3);
+        QKV + (size_t)(qrow0 + lr) * ld + (g * G + col % G) * HD + ((slot ^ cswz(col)) << 3);
     load_lds16(src, ldsQ + (c - lane) * 8);
   }
 
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
           const uint16_t* page = b.kv + (int64_t)pg * b.page_stride;
           src = page + (isv ? kPageRows * Hkv * HD : 0) + (size_t)(kr % kPageRows) * (Hkv * HD) + g * HD + dc * 8;
         } else {
-          src = seq_base + (size_t)kr * ld + (isv ? vcol : kcol) + dc * 8;
+          src = QKV + (size_t)(item.koff + kr) * ld + (isv ? vcol : kcol) + dc * 8;
         }
         lds_u16_t* dst = (isv ? dV : dK) + (isv ? ins - NLI : ins) * KPI * HD;
         load_lds16(src, dst);
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
       const int c = (isv ? ins - sin : ins) * 64 + lane;
       const int r = c / CPR, slot = c % CPR;
       const int lr = min(r, item_nrows - 1);
-      const uint16_t* src = seq_base + (size_t)(item_row0 + lr) * ld + (isv ? vcol : kcol) + ((slot ^ cswz(r)) << 3);
+      const uint16_t* src = QKV + (size_t)(qrow0 + lr) * ld + (isv ? vcol : kcol) + ((slot ^ cswz(r)) << 3);
       load_lds16(src, ldsQ + (isv ? rows_per_item * HD : 0) + (c - lane) * 8);
     }
   };
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   }
   __syncthreads();
   // rows of the item: G heads x HD contiguous per row, 16 bytes per lane
-  uint16_t* const obase = O + (size_t)(sd.row_off + item_row0) * ldo + g * G * HD;
+  uint16_t* const obase = O + (size_t)qrow0 * ldo + g * G * HD;
 #pragma unroll
   for (int j = 0; j < QCH / (64 * NW); ++j) {
     const int c = (wave + j * NW) * 64 + lane;

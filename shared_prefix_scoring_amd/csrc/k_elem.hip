@@ -25,14 +25,10 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, 
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= T) return;
-  // sequence holding this row: last s with seq_row_off[s] <= row
-  int lo = 0, hi = b.hdr->n_seq - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (b.seq_row_off[mid] <= row) lo = mid; else hi = mid - 1;
-  }
-  const SeqDesc sd = b.seqs[lo];
-  const int rho = row - sd.row_off;
+  const int n = b.hdr->n_seq;
+  const int seg = packed_segment(b.seq_row_off, 2 * n, row);  // branch segments first, then prefix ones
+  const SeqDesc sd = b.seqs[seg < n ? seg : seg - n];
+  const int rho = row - (seg < n ? sd.boff : sd.row_off);
   const int id = rho < sd.id_len ? ids[sd.id_off + rho] : ids[sd.cand_id_off + (rho - sd.id_len)];
   if (lane == 0) pos[row] = rho < sd.L ? rho : sd.L + (rho - sd.L) % sd.M;
   float* xr = X + (size_t)row * d;
@@ -79,11 +75,11 @@ void launch_embed(hipStream_t s, int cap_rows, const int32_t* ids, DevBatch b, c
 // and the scaling (NQ float4 per lane; NQ = 0 loops over the row instead).
 template <int NQ>
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ X, const float* __restrict__ g,
-                                                 uint16_t* __restrict__ Y, const CallHeader* __restrict__ hdr,
+                                                 uint16_t* __restrict__ Y, const int32_t* __restrict__ n_rows,
                                                  int d, float eps) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= hdr->T) return;
+  if (row >= *n_rows) return;
   const float4* xr = reinterpret_cast<const float4*>(X + (size_t)row * d);
   const float4* gr = reinterpret_cast<const float4*>(g);
   uint2* yr = reinterpret_cast<uint2*>(Y + (size_t)row * d);
@@ -124,12 +120,12 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ X, co
 }
 
 void launch_rmsnorm(hipStream_t s, int cap_rows, const float* X, const float* g, uint16_t* Y,
-                    const CallHeader* hdr, int d, float eps) {
+                    const int32_t* n_rows, int d, float eps) {
   if (cap_rows <= 0) return;
   const dim3 grid((cap_rows + 3) / 4), blk(256);
-  if (d == 1024) hipLaunchKernelGGL(k_rmsnorm<4>, grid, blk, 0, s, X, g, Y, hdr, d, eps);
-  else if (d == 2048) hipLaunchKernelGGL(k_rmsnorm<8>, grid, blk, 0, s, X, g, Y, hdr, d, eps);
-  else hipLaunchKernelGGL(k_rmsnorm<0>, grid, blk, 0, s, X, g, Y, hdr, d, eps);
+  if (d == 1024) hipLaunchKernelGGL(k_rmsnorm<4>, grid, blk, 0, s, X, g, Y, n_rows, d, eps);
+  else if (d == 2048) hipLaunchKernelGGL(k_rmsnorm<8>, grid, blk, 0, s, X, g, Y, n_rows, d, eps);
+  else hipLaunchKernelGGL(k_rmsnorm<0>, grid, blk, 0, s, X, g, Y, n_rows, d, eps);
 }
 
 // ---------------------------------------------------------------------------
@@ -259,14 +255,12 @@ __global__ __launch_bounds__(256) void k_kv_store(const uint16_t* __restrict__ Q
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= T) return;
-  int lo = 0, hi = b.hdr->n_seq - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (b.seq_row_off[mid] <= row) lo = mid; else hi = mid - 1;
-  }
-  const SeqDesc sd = b.seqs[lo];
+  const int n = b.hdr->n_seq;
+  const int seg = packed_segment(b.seq_row_off, 2 * n, row);
+  if (seg < n) return;  // a branch row
+  const SeqDesc sd = b.seqs[seg - n];
   const int rho = row - sd.row_off;
-  if (sd.pt < 0 || rho >= sd.L) return;  // not a session sequence, or a branch row
+  if (sd.pt < 0) return;  // not a session sequence
   const int kvw = Hkv * hd;
   const int pg = b.pages[sd.pt + rho / kPageRows];
   uint16_t* dst = b.kv + (int64_t)pg * b.page_stride + (size_t)(rho % kPageRows) * kvw;

@@ -10,7 +10,7 @@ namespace duolm {
 // Device views of one launch's batch description.
 struct DevBatch {
   const CallHeader* hdr;
-  const int32_t* seq_row_off;  // [n_seq + 1] first row of each sequence, then T
+  const int32_t* seq_row_off;  // [2 n_seq + 1]: each sequence's first branch row, each one's first prefix row, T
   const SeqDesc* seqs;
   const WorkItem* pitems;
   const WorkItem* bitems;
@@ -28,8 +28,9 @@ struct DevBatch {
 void launch_embed(hipStream_t s, int cap_rows, const int32_t* ids, DevBatch b, const uint16_t* E,
                   const uint16_t* D, const uint16_t* Dinl, int V, int64_t n_vid, int d, float* X,
                   int32_t* pos);
+// rows [0, *n_rows)
 void launch_rmsnorm(hipStream_t s, int cap_rows, const float* X, const float* g, uint16_t* Y,
-                    const CallHeader* hdr, int d, float eps);
+                    const int32_t* n_rows, int d, float eps);
 void launch_qk_rope(hipStream_t s, int cap_rows, uint16_t* QKV, int ld, const CallHeader* hdr,
                     const int32_t* pos, const float* gq, const float* gk, const float2* rope, int H,
                     int Hkv, int hd, float eps);
