@@ -124,6 +124,9 @@ typedef struct {
   int32_t mode;      /* duolm_mode */
   int32_t use_graph; /* nonzero: replay a captured HIP graph for the batch's shape bucket */
   void* hip_stream;  /* hipStream_t to order the work on, or NULL for the handle's own stream */
+  int32_t max_lanes; /* 0 or 2: a call of >= 2048 rows over >= 2 sequences runs as two halves side
+                        by side on two streams (the second is the handle's own); 1: one launch */
+  int32_t reserved;  /* 0 */
 } duolm_opts;
 
 /*
@@ -341,7 +344,9 @@ typedef enum {
 
 typedef struct {
   int64_t launches;   /* launches timed since the last reset */
-  double total_ms;    /* sum of their HIP-event durations */
+  double total_ms;    /* device time they ran: per call, the union of their intervals between HIP
+                         events (the sum of their durations unless launches overlap, as the two
+                         concurrent halves of a large batch do) */
   double flops;       /* algorithmic FLOPs of those launches (useful work only) */
   double bytes;       /* algorithmic HBM bytes of those launches */
 } duolm_kernel_stats;
@@ -349,7 +354,10 @@ typedef struct {
 /*
  * Time launches of the kernel classes in `class_mask` (bit i = class i) with
  * HIP events recorded on the launching stream, eager or inside captured
- * graphs.  0 turns timing off.  Resets the counters.
+ * graphs (as event-record nodes).  0 turns timing off.  Resets the counters.
+ * A call of at least 2048 rows over two or more sequences runs as two
+ * halves on two streams, side by side; its timed launches of one class may
+ * then overlap, and total_ms counts the time they ran once.
  */
 int duolm_set_profiling(duolm_ranker* r, uint32_t class_mask);
 int duolm_get_kernel_stats(duolm_ranker* r, int32_t kernel_class, duolm_kernel_stats* out);

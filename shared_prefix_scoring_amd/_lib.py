@@ -52,7 +52,8 @@ class duolm_request(C.Structure):
 
 
 class duolm_opts(C.Structure):
-    _fields_ = [("mode", C.c_int32), ("use_graph", C.c_int32), ("hip_stream", C.c_void_p)]
+    _fields_ = [("mode", C.c_int32), ("use_graph", C.c_int32), ("hip_stream", C.c_void_p),
+                ("max_lanes", C.c_int32), ("reserved", C.c_int32)]
 
 
 class duolm_template(C.Structure):
@@ -176,8 +177,8 @@ def _requests(reqs: Sequence[Tuple], cand_len=None):
     return arr, keep
 
 
-def _opts(mode: int, use_graph: bool, stream) -> duolm_opts:
-    return duolm_opts(int(mode), 1 if use_graph else 0, C.c_void_p(stream or 0))
+def _opts(mode: int, use_graph: bool, stream, max_lanes: int = 0) -> duolm_opts:
+    return duolm_opts(int(mode), 1 if use_graph else 0, C.c_void_p(stream or 0), int(max_lanes), 0)
 
 
 # ----------------------------------------------------------------- entry points
@@ -209,21 +210,21 @@ def duolm_get_dims(r) -> duolm_dims:
 
 
 def duolm_score_batch(r, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None,
-                      cand_len=None) -> np.ndarray:
+                      cand_len=None, max_lanes: int = 0) -> np.ndarray:
     arr, keep = _requests(reqs, cand_len)
     n = sum(int(arr[i].n_cand) for i in range(len(reqs)))
     out = np.empty(n, dtype=np.float32)
-    o = _opts(mode, use_graph, stream)
+    o = _opts(mode, use_graph, stream, max_lanes)
     _check(lib().duolm_score_batch(r, arr, len(reqs), out.ctypes.data, C.byref(o)))
     del keep
     return out
 
 
 def duolm_score_batch_dev(r, prefix_len, n_cand, d_ids: int, d_scores: int, mode: int = DUOLM_MODE_MIS,
-                          use_graph: bool = True, stream=None, cand_len=None) -> None:
+                          use_graph: bool = True, stream=None, cand_len=None, max_lanes: int = 0) -> None:
     L, K = _i32(prefix_len), _i32(n_cand)
     M = None if cand_len is None else _cand_lens(L.shape[0], cand_len)
-    o = _opts(mode, use_graph, stream)
+    o = _opts(mode, use_graph, stream, max_lanes)
     _check(lib().duolm_score_batch_dev(r, L.ctypes.data, K.ctypes.data, None if M is None else M.ctypes.data,
                                        L.shape[0], C.c_void_p(d_ids), C.c_void_p(d_scores), C.byref(o)))
 
@@ -340,12 +341,12 @@ def duolm_pack_requests(p: PackInput, n_threads: int = 1, ids: np.ndarray | None
 
 
 def duolm_score_packed(r, prefix_len, n_cand, cand_len, ids, mode: int = DUOLM_MODE_MIS, use_graph: bool = True,
-                       stream=None) -> np.ndarray:
+                       stream=None, max_lanes: int = 0) -> np.ndarray:
     L, K = _i32(prefix_len), _i32(n_cand)
     M = None if cand_len is None else _i32(cand_len)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     out = np.empty(int(K.sum()), dtype=np.float32)
-    o = _opts(mode, use_graph, stream)
+    o = _opts(mode, use_graph, stream, max_lanes)
     _check(lib().duolm_score_packed(r, L.ctypes.data, K.ctypes.data, None if M is None else M.ctypes.data,
                                     L.shape[0], ids.ctypes.data, out.ctypes.data, C.byref(o)))
     return out
@@ -378,7 +379,7 @@ def duolm_session_free(s) -> None:
 
 
 def duolm_session_step(r, sessions, new_ids, cands=None, cand_len=None, mode: int = DUOLM_MODE_MIS,
-                       use_graph: bool = True, stream=None) -> np.ndarray:
+                       use_graph: bool = True, stream=None, max_lanes: int = 0) -> np.ndarray:
     """sessions: handles; new_ids[i]: ids appended to session i (may be empty);
     cands[i]: its candidate ids (empty or None: none), cand_len as in score()."""
     n = len(sessions)
@@ -393,7 +394,7 @@ def duolm_session_step(r, sessions, new_ids, cands=None, cand_len=None, mode: in
     ids = np.ascontiguousarray(np.concatenate(parts) if parts else np.zeros(0, np.int32), dtype=np.int32)
     hs = (C.c_void_p * n)(*[s.value if isinstance(s, C.c_void_p) else s for s in sessions])
     out = np.empty(int(n_cand.sum()), dtype=np.float32)
-    o = _opts(mode, use_graph, stream)
+    o = _opts(mode, use_graph, stream, max_lanes)
     _check(lib().duolm_session_step(r, hs, n, n_new.ctypes.data, n_cand.ctypes.data,
                                     None if cand_len is None else M.ctypes.data,
                                     ids.ctypes.data if ids.size else None, out.ctypes.data if out.size else None,
@@ -451,16 +452,17 @@ class Ranker:
         return duolm_reference_scale(self.h)
 
     def score(self, reqs, mode: int = DUOLM_MODE_MIS, use_graph: bool = True, stream=None,
-              cand_len=None) -> np.ndarray:
-        return duolm_score_batch(self.h, reqs, mode, use_graph, stream, cand_len)
+              cand_len=None, max_lanes: int = 0) -> np.ndarray:
+        return duolm_score_batch(self.h, reqs, mode, use_graph, stream, cand_len, max_lanes)
 
     def score_packed(self, prefix_len, n_cand, cand_len, ids, mode: int = DUOLM_MODE_MIS,
-                     use_graph: bool = True, stream=None) -> np.ndarray:
-        return duolm_score_packed(self.h, prefix_len, n_cand, cand_len, ids, mode, use_graph, stream)
+                     use_graph: bool = True, stream=None, max_lanes: int = 0) -> np.ndarray:
+        return duolm_score_packed(self.h, prefix_len, n_cand, cand_len, ids, mode, use_graph, stream, max_lanes)
 
     def score_dev(self, prefix_len, n_cand, d_ids: int, d_scores: int, mode: int = DUOLM_MODE_MIS,
-                  use_graph: bool = True, stream=None, cand_len=None) -> None:
-        duolm_score_batch_dev(self.h, prefix_len, n_cand, d_ids, d_scores, mode, use_graph, stream, cand_len)
+                  use_graph: bool = True, stream=None, cand_len=None, max_lanes: int = 0) -> None:
+        duolm_score_batch_dev(self.h, prefix_len, n_cand, d_ids, d_scores, mode, use_graph, stream, cand_len,
+                              max_lanes)
 
     def stage(self, reqs, layer: int, stage: str, mode: int = DUOLM_MODE_MIS, cand_len=None) -> np.ndarray:
         d = self.dims
@@ -497,9 +499,9 @@ class Ranker:
         return Session(self)
 
     def step(self, sessions, new_ids, cands=None, cand_len=None, use_graph: bool = True, stream=None,
-             mode: int = DUOLM_MODE_MIS) -> np.ndarray:
+             mode: int = DUOLM_MODE_MIS, max_lanes: int = 0) -> np.ndarray:
         return duolm_session_step(self.h, [x.h for x in sessions], new_ids, cands, cand_len, mode, use_graph,
-                                  stream)
+                                  stream, max_lanes)
 
     def close(self) -> None:
         if self.h:
