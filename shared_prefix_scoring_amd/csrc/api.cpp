@@ -88,7 +88,13 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // graph's grids exceed the true sizes by at most 1/16 (the GEMM tile choice
 // is made on these bounds).
 int bucket(int x) {
-  if (x <= 32) return x <= 0 ? 0 : 32;
+  // small counts round to a power of two: a graph's grids are sized by these
+  // caps, and each surplus attention workgroup still takes a CU slot to exit
+  if (x <= 32) {
+    int p = x <= 0 ? 0 : 1;
+    while (p < x) p <<= 1;
+    return p;
+  }
   int e = 0;
   while ((x >> e) >= 32) ++e;
   int m = (x + (1 << e) - 1) >> e;
