@@ -157,7 +157,10 @@ struct GraphEntry {
 // round of its GEMMs leave CUs idle that the other half's kernels fill (a
 // 64-request batch as two concurrent halves took 26.1 ms against 28.3 ms as
 // one launch, measured with two handles).
-constexpr int kLanes = 2;
+#ifndef DUOLM_LANES
+#define DUOLM_LANES 2
+#endif
+constexpr int kLanes = DUOLM_LANES;
 struct Lane {
   hipStream_t stream = nullptr;  // lane 1: its own stream; lane 0 runs on the call's stream
   hipEvent_t done = nullptr;     // lane 1 finished the call's launches
@@ -1010,23 +1013,26 @@ int validate_lengths(duolm_ranker* R, const CallInput& in, int64_t& total_ids, i
 }
 
 // Split the call into launches of at most max_rows rows.
-// Where a call's sequences are cut into launches: at the row limit, and once
-// at half the rows when the call is large enough to run as two concurrent
-// halves (one per lane).
+// Where a call's sequences are cut into launches: at the row limit, and --
+// when the call is large enough to run as concurrent pieces, one per lane --
+// at sequence boundaries near each 1/kLanes of its rows.
 struct Splitter {
   duolm_ranker* R;
   int64_t total;
-  bool halves, cut = false;
+  int pieces, cuts = 0;
+  int64_t done = 0;  // rows in the closed launches
   Splitter(duolm_ranker* r, int64_t total_rows, int64_t n_seqs, bool lanes = true)
       : R(r), total(total_rows),
-        halves(lanes && kLanes > 1 && n_seqs >= 2 && total_rows >= kLaneMinRows && total_rows <= r->max_rows) {}
+        pieces(lanes && n_seqs >= 2 && total_rows >= kLaneMinRows && total_rows <= r->max_rows
+                   ? (int)std::min<int64_t>(kLanes, n_seqs) : 1) {}
   // before adding a sequence of `rows` rows; score_next is its first score
   void before(std::vector<Plan>& plans, int64_t rows, int score_next) {
     const Plan& P = plans.back();
     const bool full = P.T > 0 && P.T + rows > R->max_rows;
-    const bool half = halves && !cut && P.T > 0 && 2 * (int64_t)P.T >= total;
-    if (!full && !half) return;
-    if (half) cut = true;
+    const bool piece = cuts + 1 < pieces && P.T > 0 && (done + P.T) * pieces >= total * (cuts + 1);
+    if (!full && !piece) return;
+    if (piece) ++cuts;
+    done += P.T;
     plan_close(R, plans.back());
     plans.emplace_back();
     plans.back().score_off = score_next;
@@ -1098,8 +1104,8 @@ int run_plans(duolm_ranker* R, const std::vector<Plan>& plans, const int32_t* id
               float* out, bool out_dev, int64_t total_scores, hipStream_t s, bool use_graph,
               const uint16_t* inline_rows = nullptr, int64_t n_inline = 0) {
   int rc;
-  // plan i runs on lane i % nl: lane 0 on the call's stream, lane 1 on its own
-  const int nl = plans.size() > 1 ? kLanes : 1;
+  // plan i runs on lane i % nl: lane 0 on the call's stream, the others on their own
+  const int nl = (int)std::min<size_t>(plans.size(), kLanes);
   for (int li = 0; li < nl; ++li) {
     int maxT = 0, mseq = 0, mpi = 0, mbi = 0, mhs = 0, mpt = 0;
     for (size_t i = li; i < plans.size(); i += nl) {
@@ -1126,9 +1132,9 @@ int run_plans(duolm_ranker* R, const std::vector<Plan>& plans, const int32_t* id
                            ids_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s));
   *R->h_err = 0;
   HIP_TRY(hipMemcpyAsync(R->d_err, R->h_err, 4, hipMemcpyHostToDevice, s));
-  if (nl > 1) {  // lane 1 starts once the ids and the error flag are on the device
+  if (nl > 1) {  // the other lanes start once the ids and the error flag are on the device
     HIP_TRY(hipEventRecord(R->ids_ready, s));
-    HIP_TRY(hipStreamWaitEvent(R->lanes[1].stream, R->ids_ready, 0));
+    for (int li = 1; li < nl; ++li) HIP_TRY(hipStreamWaitEvent(R->lanes[li].stream, R->ids_ready, 0));
   }
   R->ev_used = 0;
   if (R->prof_mask) HIP_TRY(hipEventRecord(R->call_t0, s));  // the call's timeline origin (before lane 1 forks)
@@ -1150,9 +1156,9 @@ int run_plans(duolm_ranker* R, const std::vector<Plan>& plans, const int32_t* id
       return rc;
     }
   }
-  if (nl > 1) {
-    HIP_TRY(hipEventRecord(R->lanes[1].done, R->lanes[1].stream));
-    HIP_TRY(hipStreamWaitEvent(s, R->lanes[1].done, 0));
+  for (int li = 1; li < nl; ++li) {
+    HIP_TRY(hipEventRecord(R->lanes[li].done, R->lanes[li].stream));
+    HIP_TRY(hipStreamWaitEvent(s, R->lanes[li].done, 0));
   }
   HIP_TRY(hipMemcpyAsync(R->h_err, R->d_err, 4, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
