@@ -129,9 +129,10 @@ struct Plan {
 
 struct Caps {
   int T, seq, pitems, bitems, scores, pages, session, brows;
+  int share;  // launches of the call running side by side (GEMM tile choice)
   bool operator<(const Caps& o) const {
-    return std::tie(T, seq, pitems, bitems, scores, pages, session, brows) <
-           std::tie(o.T, o.seq, o.pitems, o.bitems, o.scores, o.pages, o.session, o.brows);
+    return std::tie(T, seq, pitems, bitems, scores, pages, session, brows, share) <
+           std::tie(o.T, o.seq, o.pitems, o.bitems, o.scores, o.pages, o.session, o.brows, o.share);
   }
 };
 
@@ -789,7 +790,8 @@ void enqueue_forward(Enq& q, const Caps& c) {
     q.brows = false;
     q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, c.T, ln->X, W.attn_norm, ln->Xn, dT, d, eps); });
     if (q.stop(l, DUOLM_STAGE_ATTN_NORM)) return;
-    q.run(DUOLM_K_GEMM_QKV, [&] { launch_gemm(s, EPI_BF16, c.T, ln->Xn, d, W.wqkv, d, ln->QKV, nq, dT, nq, d); });
+    q.run(DUOLM_K_GEMM_QKV,
+          [&] { launch_gemm(s, EPI_BF16, c.T, ln->Xn, d, W.wqkv, d, ln->QKV, nq, dT, nq, d, c.share); });
     if (q.stop(l, DUOLM_STAGE_QKV)) return;
     q.run(DUOLM_K_QK_ROPE, [&] {
       launch_qk_rope(s, c.T, ln->QKV, nq, b.hdr, ln->pos, W.q_norm, W.k_norm, R->rope, H, Hk, hd, eps);
@@ -818,13 +820,16 @@ void enqueue_forward(Enq& q, const Caps& c) {
     const int cr = tail ? c.brows : c.T;  // rows (cap) of the rest of the layer
     const int32_t* dR = tail ? dB : dT;
     q.brows = tail;
-    q.run(DUOLM_K_GEMM_O, [&] { launch_gemm(s, EPI_RESID, cr, ln->Ob, H * hd, W.wo, H * hd, ln->X, d, dR, d, H * hd); });
+    q.run(DUOLM_K_GEMM_O,
+          [&] { launch_gemm(s, EPI_RESID, cr, ln->Ob, H * hd, W.wo, H * hd, ln->X, d, dR, d, H * hd, c.share); });
     if (q.stop(l, DUOLM_STAGE_ATTN_RESID)) return;
     q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, cr, ln->X, W.mlp_norm, ln->Xn, dR, d, eps); });
     if (q.stop(l, DUOLM_STAGE_MLP_NORM)) return;
-    q.run(DUOLM_K_GEMM_GATEUP, [&] { launch_gemm(s, EPI_SWIGLU, cr, ln->Xn, d, W.wgu, d, ln->Hb, F, dR, 2 * F, d); });
+    q.run(DUOLM_K_GEMM_GATEUP,
+          [&] { launch_gemm(s, EPI_SWIGLU, cr, ln->Xn, d, W.wgu, d, ln->Hb, F, dR, 2 * F, d, c.share); });
     if (q.stop(l, DUOLM_STAGE_SWIGLU)) return;
-    q.run(DUOLM_K_GEMM_DOWN, [&] { launch_gemm(s, EPI_RESID, cr, ln->Hb, F, W.wdown, F, ln->X, d, dR, d, F); });
+    q.run(DUOLM_K_GEMM_DOWN,
+          [&] { launch_gemm(s, EPI_RESID, cr, ln->Hb, F, W.wdown, F, ln->X, d, dR, d, F, c.share); });
     q.brows = false;
     if (q.stop(l, DUOLM_STAGE_LAYER_OUT)) return;
   }
@@ -923,12 +928,13 @@ void settle_spans(duolm_ranker* R, std::vector<Span>& spans) {
 }
 
 // Run one planned launch: upload, then eager enqueue or graph replay.
-int run_launch(duolm_ranker* R, Lane& Ln, const Plan& P, hipStream_t s, bool use_graph, std::vector<Timed>* timed) {
+int run_launch(duolm_ranker* R, Lane& Ln, const Plan& P, hipStream_t s, bool use_graph, std::vector<Timed>* timed,
+               int share) {
   int rc = upload_plan(R, Ln, P, s);
   if (rc) return rc;
   if (!use_graph) {
     Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(),
-           (int)P.pages.size(), P.session ? 1 : 0, P.TB};
+           (int)P.pages.size(), P.session ? 1 : 0, P.TB, share};
     Enq q{R, &Ln, s, R->prof_mask ? timed : nullptr, nullptr};
     enqueue_forward(q, c);
     HIP_TRY(hipGetLastError());
@@ -937,7 +943,7 @@ int run_launch(duolm_ranker* R, Lane& Ln, const Plan& P, hipStream_t s, bool use
   Caps c{std::min(bucket(P.T), Ln.cap_T), std::min(bucket((int)P.seqs.size()), Ln.cap_seq),
          std::min(bucket((int)P.pitems.size()), Ln.cap_pi), std::min(bucket((int)P.bitems.size()), Ln.cap_bi),
          std::min(bucket((int)P.head_rows.size()), Ln.cap_hs), 0, P.session ? 1 : 0,
-         std::min(bucket(P.TB), Ln.cap_T)};
+         std::min(bucket(P.TB), Ln.cap_T), share};
   auto it = Ln.graphs.find(c);
   if (it == Ln.graphs.end()) {
     GraphEntry ge;
@@ -1150,7 +1156,7 @@ int run_plans(duolm_ranker* R, const std::vector<Plan>& plans, const int32_t* id
       add_stats(R, plans[i - nl], timed[i - nl], spans);
       timed[i - nl].clear();
     }
-    if ((rc = run_launch(R, Ln, plans[i], ls, use_graph, &timed[i]))) {
+    if ((rc = run_launch(R, Ln, plans[i], ls, use_graph, &timed[i], nl))) {
       (void)sync_all(R);
       (void)hipStreamSynchronize(s);
       return rc;
@@ -1800,7 +1806,7 @@ int duolm_debug_forward(duolm_ranker* R, const duolm_request* reqs, int32_t n_re
   *R->h_err = 0;
   HIP_TRY(hipMemcpyAsync(R->d_err, R->h_err, 4, hipMemcpyHostToDevice, s));
   if ((rc = upload_plan(R, L0, P, s))) return rc;
-  Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(), 0, 0, P.TB};
+  Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(), 0, 0, P.TB, 1};
   Enq q{R, &L0, s, nullptr, nullptr};
   q.stop_layer = layer == D.n_layers ? D.n_layers - 1 : layer;
   q.stop_stage = buf_stage;

@@ -44,9 +44,11 @@ void launch_kv_store(hipStream_t s, int cap_rows, const uint16_t* QKV, int ld, D
 // GEMM epilogues
 enum { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 // C = epi(A[M,K] W[N,K]^T); M read from *dM (<= cap_m).  Returns false if the
-// shape is unsupported (N % 64 or K % 64 nonzero).
+// shape is unsupported (N % 64 or K % 64 nonzero).  share: launches running
+// side by side on the chip (each counts 1/share of the CUs when the tile
+// size is chosen).
 bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W,
-                 int ldw, void* C, int ldc, const int32_t* dM, int N, int K);
+                 int ldw, void* C, int ldc, const int32_t* dM, int N, int K, int share = 1);
 
 // Attention over one launch's work items.  Returns rows covered per item.
 int attn_rows_per_item(bool branch, int group);
