@@ -144,3 +144,20 @@ def test_session_errors(gpu_tiny, tiny):
         assert ei.value.code == -6
     finally:
         r2.close()
+
+
+def test_sessions_in_two_lanes_equal_one(gpu_qwen):
+    # a step over many users runs as two concurrent halves; one launch gives
+    # the same bits
+    cfg, _, _, _, r = gpu_qwen
+    r.kv_pool_init(64 * 512)
+    reqs = synth.make_requests(3, cfg, n_requests=12, seed=90)
+    a = [r.session() for _ in reqs]
+    b = [r.session() for _ in reqs]
+    try:
+        got_a = r.step(a, [q.prefix for q in reqs], [q.cands for q in reqs])
+        got_b = r.step(b, [q.prefix for q in reqs], [q.cands for q in reqs], max_lanes=1)
+        np.testing.assert_array_equal(got_a, got_b)
+    finally:
+        for x in a + b:
+            x.close()
