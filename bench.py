@@ -289,21 +289,27 @@ def bench_multivec(ranker, cfg, rounds):
 def bench_stress(ranker, cfg, n_req, n_ind):
     """L=4096, K=512: MIS over n_req requests in one call, against independent
     scoring (prefix replicated per candidate, full causal forward) of the
-    first n_ind candidates of the first two requests."""
+    first n_ind candidates of the first two requests (median call times)."""
     import torch
     import synth
     reqs = synth.make_requests(5, cfg, n_requests=n_req)
     mis_in = [(r.prefix, r.cands) for r in reqs]
     ranker.score(mis_in)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    mis = ranker.score(mis_in)
-    t_mis = time.perf_counter() - t0
+    ts = []
+    for _ in range(5):  # median of five calls
+        t0 = time.perf_counter()
+        mis = ranker.score(mis_in)
+        ts.append(time.perf_counter() - t0)
+    t_mis = float(np.median(ts))
     ind_in = [(r.prefix, r.cands[:n_ind]) for r in reqs[:2]]
     ranker.score(ind_in, mode=1)
-    t0 = time.perf_counter()
-    ind = ranker.score(ind_in, mode=1)
-    t_ind = time.perf_counter() - t0
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        ind = ranker.score(ind_in, mode=1)
+        ts.append(time.perf_counter() - t0)
+    t_ind = float(np.median(ts))
     ref = np.concatenate([mis[i * 512:i * 512 + n_ind] for i in range(2)])
     rate_mis = len(mis) / t_mis
     rate_ind = len(ind) / t_ind
