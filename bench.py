@@ -467,9 +467,14 @@ def summarize_traffic(out_dir, warmup, steps, pool_size):
     # every eager call of the run, in order: warmup and timed steps, the pass
     # without kernel timing, the branch-attention pass
     seq = list(range(calls)) + list(range(warmup, calls)) + list(range(warmup, min(calls, warmup + 10)))
-    rows = [sum(r.L + r.K for r in pool[i * 64:(i + 1) * 64]) for i in seq]
-    if len(rows) * cfg.n_layers != n:
-        raise SystemExit(f"{n} gate/up dispatches counted, {len(rows) * cfg.n_layers} expected from the call sequence")
+    # each call: n_layers - 1 launches over all its rows, and the last layer's
+    # over the branch rows alone
+    rows = []
+    for i in seq:
+        reqs = pool[i * 64:(i + 1) * 64]
+        rows += [sum(r.L + r.K for r in reqs)] * (cfg.n_layers - 1) + [sum(r.K for r in reqs)]
+    if len(rows) != n:
+        raise SystemExit(f"{n} gate/up dispatches counted, {len(rows)} expected from the call sequence")
     t_mean = sum(rows) / len(rows)
     d, f = cfg.d_model, cfg.d_ffn
     alg = 2 * f * d * 2 + t_mean * (d * 2 + f * 2)  # weights + activations in + SwiGLU out (bf16)
@@ -477,7 +482,7 @@ def summarize_traffic(out_dir, warmup, steps, pool_size):
     out = {
         "kernel": "k_gemm<256, 256, 4, 2, EPI_SWIGLU> (gate/up projection + SwiGLU epilogue)",
         "workload": f"bench.py workload: 0.6B-shaped ranker, 64 requests x 100 candidates per call, eager launches, "
-                    f"{calls} calls x {cfg.n_layers} layers",
+                    f"{len(seq)} calls x {cfg.n_layers} layers",
         "commands": [
             "cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'k_gemm|k_copy' -d $REPO/gpurun_out/traffic/tr_f "
             f"-o f -f csv -- python -u $REPO/bench.py --steps {steps} --warmup {warmup} --no-graph --max-lanes 1 --cpu-baseline-s 0 --open-loop 0",
@@ -508,6 +513,82 @@ def summarize_traffic(out_dir, warmup, steps, pool_size):
     print(json.dumps(out), flush=True)
 
 
+def summarize_trace(trace_dir, steps, C):
+    """Per-kernel summary of a rocprofv3 --kernel-trace run of the headline
+    bench (markdown rows on stdout): dispatches, average duration, the union of
+    the dispatch intervals (device time the kernel ran, counting concurrent
+    dispatches once), and the average over dispatches that ran alone (no other
+    dispatch overlapping them).  Then the gate/up GEMM by launch size, and its
+    average over the one-lane timed region alone, the launches the bench's HIP
+    events time: a one-launch call ends with a gate/up launch over its C x 100
+    branch rows, and the bench runs `steps` such calls to prime the graphs,
+    then the `steps` timed ones."""
+    import csv
+    rows = []
+    for root, _, files in os.walk(trace_dir):
+        for fn in files:
+            if fn.endswith("kernel_trace.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    rows += list(csv.DictReader(f))
+    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
+    grids = {}
+    for r in rows:  # the gate/up GEMM by launch size (grid blocks)
+        if "k_gemm<256, 256, 4, 2, 2," in r["Kernel_Name"]:
+            blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+            grids.setdefault(blocks, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    alone = []
+    hi = -1  # latest end among earlier dispatches
+    for i, (a, b, _) in enumerate(ev):
+        nxt = ev[i + 1][0] if i + 1 < len(ev) else b + 1
+        alone.append(a >= hi and b <= nxt)
+        hi = max(hi, b)
+
+    def short(n):
+        n = n.replace("duolm::", "").replace("(anonymous namespace)::", "").replace("void ", "")
+        return n[:n.index("(")] if "(" in n else n
+
+    stats = {}
+    for (a, b, n), solo in zip(ev, alone):
+        st = stats.setdefault(short(n), {"n": 0, "sum": 0, "iv": [], "solo": []})
+        st["n"] += 1
+        st["sum"] += b - a
+        st["iv"].append((a, b))
+        if solo:
+            st["solo"].append(b - a)
+    total = sum(st["sum"] for st in stats.values())
+    print("| kernel | dispatches | avg us | union ms | alone: dispatches, avg us | % of summed time |")
+    print("|---|---|---|---|---|---|")
+    for name, st in sorted(stats.items(), key=lambda kv: -kv[1]["sum"]):
+        u, lo, hi = 0, None, None
+        for a, b in sorted(st["iv"]):
+            if lo is None or a > hi:
+                if lo is not None:
+                    u += hi - lo
+                lo, hi = a, b
+            else:
+                hi = max(hi, b)
+        u += hi - lo
+        solo = st["solo"]
+        solo_txt = f"{len(solo)}, {sum(solo) / len(solo) / 1e3:.1f}" if solo else "0, -"
+        print(f"| `{name}` | {st['n']} | {st['sum'] / st['n'] / 1e3:.1f} | {u / 1e6:.2f} | {solo_txt} | "
+              f"{st['sum'] / total * 100:.1f} |")
+    print()
+    print("| gate/up GEMM launch size (blocks) | dispatches | avg us |")
+    print("|---|---|---|")
+    for blocks, d in sorted(grids.items(), key=lambda kv: -kv[0]):
+        print(f"| {blocks} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} |")
+    gu = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                 int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+                for r in rows if "k_gemm<256, 256, 4, 2, 2," in r["Kernel_Name"])
+    tail_blocks = -(-C * 100 // 256) * (2 * 3072 // 256)  # 256 x 256 tiles over the branch rows
+    tails = [i for i, g in enumerate(gu) if g[2] == tail_blocks]
+    if len(tails) >= 2 * steps:
+        win = gu[tails[steps - 1] + 1:tails[2 * steps - 1] + 1]
+        avg = sum(b - a for a, b, _ in win) / len(win) / 1e3
+        print()
+        print(f"one-lane timed region: {len(win)} gate/up dispatches ({steps} calls), avg {avg:.1f} us")
+
+
 def traffic_from_profile(kernel_hash):
     p = os.path.join(ROOT, "profiles", "traffic_gemm_gateup.json")
     if not os.path.exists(p):
@@ -534,6 +615,8 @@ def main():
                     help="requests in the Poisson-arrival run (0 disables it)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel class (untimed pass)")
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a per-kernel summary of a rocprofv3 --kernel-trace run under DIR (no GPU)")
     ap.add_argument("--summarize-traffic", metavar="DIR",
                     help="write profiles/traffic_gemm_gateup.json from the counter runs under DIR (no GPU)")
     ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export", "packer", "session"],
@@ -546,6 +629,9 @@ def main():
                          "prefix recompute")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.steps, args.concurrency)
+        return
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic, args.warmup, args.steps, args.pool)
         return
