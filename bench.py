@@ -454,7 +454,7 @@ def summarize_traffic(out_dir, warmup, steps, pool_size):
             raise SystemExit(f"no {counter} rows for {name_part} under {d}")
         return sum(vals) / len(vals), len(vals)
 
-    gate = "k_gemm<256, 256, 4, 2, 2,"
+    gate = "k_gemm<256, 256, 4, 2, 2>"
     f_kib, n = per_dispatch("tr_f", "FETCH_SIZE", gate)
     w_kib, _ = per_dispatch("tr_w", "WRITE_SIZE", gate)
     cf_kib, _ = per_dispatch("cal_f", "FETCH_SIZE", "k_copy")
@@ -533,7 +533,7 @@ def summarize_trace(trace_dir, steps, C):
     ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
     grids = {}
     for r in rows:  # the gate/up GEMM by launch size (grid blocks)
-        if "k_gemm<256, 256, 4, 2, 2," in r["Kernel_Name"]:
+        if "k_gemm<256, 256, 4, 2, 2>" in r["Kernel_Name"]:
             blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
             grids.setdefault(blocks, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     alone = []
@@ -579,7 +579,7 @@ def summarize_trace(trace_dir, steps, C):
         print(f"| {blocks} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} |")
     gu = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
                  int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
-                for r in rows if "k_gemm<256, 256, 4, 2, 2," in r["Kernel_Name"])
+                for r in rows if "k_gemm<256, 256, 4, 2, 2>" in r["Kernel_Name"])
     tail_blocks = -(-C * 100 // 256) * (2 * 3072 // 256)  # 256 x 256 tiles over the branch rows
     tails = [i for i, g in enumerate(gu) if g[2] == tail_blocks]
     if len(tails) >= 2 * steps:

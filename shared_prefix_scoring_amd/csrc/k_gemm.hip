@@ -18,7 +18,13 @@
 //     belongs at its LDS slot -- so the 32 rows of a fragment read hit
 //     distinct bank groups;
 //   * fragments are double-buffered in registers: the ds_read_b128s of k-step
-//     ks+1 are issued before the MFMAs of k-step ks;
+//     ks+1 are issued among the MFMAs of k-step ks, in a fixed instruction
+//     order held by scheduling fences (see the slab below);
+//   * the global->LDS loads are written as inline asm: while the compiler's
+//     own form of this load is in flight, it turns every fragment wait into
+//     a wait for all outstanding LDS traffic; with the loads out of its view
+//     each k-step waits only for the fragments its first MFMAs need, and the
+//     kernel waits for the loads itself (vmcnt) before the stage barrier;
 //   * the k loop order is fixed and there is no split-K, so every output row
 //     is computed by the same instruction sequence whatever M is or where the
 //     row sits: results are batch invariant;
@@ -39,14 +45,18 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// 16 bytes per lane, global -> LDS; lane i lands at lds + 16 i
+// 16 bytes per lane, global -> LDS; lane i lands at lds + 16 i.  M0 holds the
+// wave's LDS destination; one wait state separates the M0 write from the load
+// that reads it.  Nothing is returned to registers: the caller waits with
+// s_waitcnt vmcnt before the barrier that publishes the stage.
 __device__ __forceinline__ void load_lds16(const uint16_t* g, lds_u16_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+  const uint32_t base = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(base) : "memory");
 }
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool SCHED>
+template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restrict__ A, int lda,
                                                       const uint16_t* __restrict__ W, int ldw,
                                                       void* __restrict__ Cv, int ldc,
@@ -91,14 +101,6 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   }
   lds_u16_t* lds = (lds_u16_t*)(lds_void_t*)smem;
 
-  auto issue = [&](int kt, int st) {
-#pragma unroll
-    for (int j = 0; j < GA; ++j)
-      load_lds16(pa[j] + kt * BK, lds + st * STAGE + (wave + NW * j) * 8 * BK);
-#pragma unroll
-    for (int j = 0; j < GB; ++j)
-      load_lds16(pb[j] + kt * BK, lds + st * STAGE + BM * BK + (wave + NW * j) * 8 * BK);
-  };
 
   // fragment rows and their swizzles
   int a_row[MI], a_sw[MI], b_row[NI], b_sw[NI];
@@ -116,15 +118,6 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   }
 
   bf16x8_t fa[2][MI], fb[2][NI];
-  auto read_frags = [&](int st, int ks, int buf) {
-    const int kc = ks * 2 + half;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-      fa[buf][mi] = *reinterpret_cast<const bf16x8_t*>(&smem[st * STAGE + a_row[mi] + ((kc ^ a_sw[mi]) << 3)]);
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-      fb[buf][ni] = *reinterpret_cast<const bf16x8_t*>(&smem[st * STAGE + b_row[ni] + ((kc ^ b_sw[ni]) << 3)]);
-  };
 
   f32x16_t acc[MI][NI];
 #pragma unroll
@@ -134,70 +127,84 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  auto mfma_step = [&](int buf, int from, int to) {  // MFMAs number from..to-1 of one k-step
-#pragma unroll
-    for (int i = from; i < to; ++i)
-      acc[i / NI][i % NI] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i / NI], fb[buf][i % NI], acc[i / NI][i % NI], 0, 0, 0);
-  };
 
-  // One k-slab.  Program order, pinned with scheduling-group barriers:
-  //   k-steps 0..2: MFMAs of step ks interleaved with the fragment reads of
-  //   step ks+1 and with the global->LDS loads of the next slab;
-  //   k-step 3: half of its MFMAs, then the slab barrier, then the first
-  //   fragment reads of the next slab, then the other half -- so the barrier
-  //   and the LDS latency hide behind matrix work.
   constexpr int NM = MI * NI;          // MFMAs per k-step
   constexpr int NR = MI + NI;          // fragment reads per k-step
   constexpr int NG = GA + GB;          // global->LDS loads per slab
+  // fragment reads in the order the MFMAs first use them: a[0], b[0..NI-1], a[1..MI-1]
+  auto read_one = [&](int j, int st, int ks, int buf) {
+    const int kc = ks * 2 + half;
+    if (j == 0) {
+      fa[buf][0] = *reinterpret_cast<const bf16x8_t*>(&smem[st * STAGE + a_row[0] + ((kc ^ a_sw[0]) << 3)]);
+    } else if (j <= NI) {
+      const int ni = j - 1;
+      fb[buf][ni] = *reinterpret_cast<const bf16x8_t*>(&smem[st * STAGE + b_row[ni] + ((kc ^ b_sw[ni]) << 3)]);
+    } else {
+      const int mi = j - NI;
+      fa[buf][mi] = *reinterpret_cast<const bf16x8_t*>(&smem[st * STAGE + a_row[mi] + ((kc ^ a_sw[mi]) << 3)]);
+    }
+  };
+  auto issue_one = [&](int g, int kt, int st) {
+    if (g < GA)
+      load_lds16(pa[g] + kt * BK, lds + st * STAGE + (wave + NW * g) * 8 * BK);
+    else
+      load_lds16(pb[g - GA] + kt * BK, lds + st * STAGE + BM * BK + (wave + NW * (g - GA)) * 8 * BK);
+  };
+  auto mfma_one = [&](int buf, int i) {
+    acc[i / NI][i % NI] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i / NI], fb[buf][i % NI], acc[i / NI][i % NI], 0, 0, 0);
+  };
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  // One k-slab, in a fixed instruction order (scheduling fences between the
+  // groups): k-step 0 interleaves its MFMAs with the next slab's global->LDS
+  // loads and the fragment reads of k-step 1; k-steps 1 and 2 with the reads
+  // of the step after; k-step 3 runs half its MFMAs, waits for the next slab
+  // and meets the other waves at the barrier, then reads the next slab's
+  // first fragments under the other half.
   auto slab = [&](int kt, auto has_next) {
     constexpr bool NEXT = decltype(has_next)::value;
     const int st = kt & 1;
-    if constexpr (NEXT) issue(kt + 1, st ^ 1);
-    read_frags(st, 1, 1);
-    mfma_step(0, 0, NM);
-    read_frags(st, 2, 0);
-    mfma_step(1, 0, NM);
-    read_frags(st, 3, 1);
-    mfma_step(0, 0, NM);
-    mfma_step(1, 0, NM / 2);
-    // pipeline order of the region above
 #pragma unroll
-    for (int ks = 0; ks < (SCHED ? 3 : 0); ++ks) {
+    for (int ks = 0; ks < 3; ++ks) {
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      }
-      if constexpr (NEXT) {
+      for (int i = 0; i < NM; ++i) {
+        mfma_one(ks & 1, i);
+        if (ks == 0 && NEXT) {
 #pragma unroll
-        for (int i = 0; i < (NG + 2) / 3; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+          for (int g = i * NG / NM; g < (i + 1) * NG / NM; ++g) issue_one(g, kt + 1, st ^ 1);
         }
+#pragma unroll
+        for (int j = i * NR / NM; j < (i + 1) * NR / NM; ++j) read_one(j, st, ks + 1, (ks + 1) & 1);
+        fence();
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
     }
-    if constexpr (SCHED) __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
+#pragma unroll
+    for (int i = 0; i < NM / 2; ++i) {
+      mfma_one(1, i);
+      fence();
+    }
     wait_loads();
     __syncthreads();
-    if constexpr (NEXT) read_frags(st ^ 1, 0, 0);
-    mfma_step(1, NM / 2, NM);
-    if constexpr (NEXT && SCHED) {
+    fence();
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+    for (int i = NM / 2; i < NM; ++i) {
+      mfma_one(1, i);
+      if constexpr (NEXT) {
+        const int i2 = i - NM / 2;
+#pragma unroll
+        for (int j = i2 * NR / (NM / 2); j < (i2 + 1) * NR / (NM / 2); ++j) read_one(j, st ^ 1, 0, 0);
       }
+      fence();
     }
-    if constexpr (SCHED) __builtin_amdgcn_sched_group_barrier(0x008, NM, 1);
   };
 
   const int KT = K / BK;
-  issue(0, 0);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) issue_one(g, 0, 0);
   wait_loads();
   __syncthreads();
-  read_frags(0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < NR; ++j) read_one(j, 0, 0, 0);
   for (int kt = 0; kt + 1 < KT; ++kt) slab(kt, std::true_type{});
   slab(KT - 1, std::false_type{});
 
@@ -253,19 +260,19 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool SCHED>
+template <int BM, int BN, int WM, int WN>
 void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W, int ldw,
                 void* C, int ldc, const int32_t* dM, int N, int K) {
   const int grid = ((cap_m + BM - 1) / BM) * (N / BN);
   const dim3 blk(WM * WN * 64);
   if (epi == EPI_BF16)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16, SCHED>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
                        ldc, dM, N, K);
   else if (epi == EPI_RESID)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_RESID, SCHED>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_RESID>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
                        ldc, dM, N, K);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_SWIGLU, SCHED>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_SWIGLU>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
                        ldc, dM, N, K);
 }
 
@@ -304,13 +311,13 @@ bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, 
   const long tiles128 = (long)((cap_m + 127) / 128) * (N % 128 == 0 ? N / 128 : 0);
   auto row_rounds = [&](int bm) { return ((((long)cap_m + bm - 1) / bm) * nt + ncu - 1) / ncu * bm; };
   if (nt && tiles256 >= ncu && epi == EPI_RESID && row_rounds(192) < row_rounds(256))
-    launch_cfg<192, 256, 2, 4, true>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+    launch_cfg<192, 256, 2, 4>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else if (nt && tiles256 >= ncu)
-    launch_cfg<256, 256, 4, 2, true>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+    launch_cfg<256, 256, 4, 2>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else if (N % 128 == 0 && tiles128 >= 128)
-    launch_cfg<128, 128, 2, 2, false>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+    launch_cfg<128, 128, 2, 2>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else
-    launch_cfg<64, 64, 1, 1, false>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+    launch_cfg<64, 64, 1, 1>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   return true;
 }
 
