@@ -25,11 +25,16 @@
 //     a wait for all outstanding LDS traffic; with the loads out of its view
 //     each k-step waits only for the fragments its first MFMAs need, and the
 //     kernel waits for the loads itself (vmcnt) before the stage barrier;
+//   * persistent: at most one workgroup per CU, each walking the tiles
+//     blockIdx.x, + gridDim.x, ...; a tile's last slab loads the next tile's
+//     first slab into the free stage, and that load lands while the tile's
+//     epilogue runs (no relaunch, no exposed first-slab latency);
 //   * the k loop order is fixed and there is no split-K, so every output row
 //     is computed by the same instruction sequence whatever M is or where the
 //     row sits: results are batch invariant;
 //   * epilogues: bf16 store (QKV), fp32 residual add (O-proj, down-proj),
 //     SwiGLU on interleaved gate/up column blocks (gate/up projection).
+#include <algorithm>
 #include <type_traits>
 
 #include "launch.h"
@@ -73,32 +78,44 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
 
   const int M = *dM;
   const int n_tiles = N / BN;
-  const int tile_n = blockIdx.x % n_tiles;
-  const int tile_m = blockIdx.x / n_tiles;
-  const int m0 = tile_m * BM, n0 = tile_n * BN;
-  if (m0 >= M) return;
+  const int total = (M + BM - 1) / BM * n_tiles;
+  if ((int)blockIdx.x >= total) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5;
+  const int KT = K / BK;
+  const int nblk = __builtin_amdgcn_readfirstlane(gridDim.x);
 
-  // per-lane source of this wave's row groups: row g*8 + lane/8, the chunk
-  // whose swizzled slot is lane%8
+  // Load cursor: tile lt, slab lk go out next.  Per-lane source of this
+  // wave's row groups: row g*8 + lane/8, the chunk whose swizzled slot is lane%8
   const uint16_t* pa[GA];
   const uint16_t* pb[GB];
+  int lt = blockIdx.x, lk = 0;
+  auto aim = [&](int tt) {
+    const int m0 = tt / n_tiles * BM, n0 = tt % n_tiles * BN;
 #pragma unroll
-  for (int j = 0; j < GA; ++j) {
-    const int r = (wave + NW * j) * 8 + (lane >> 3);
-    const int kc = (lane & 7) ^ swz(r);
-    pa[j] = A + (size_t)min(m0 + r, M - 1) * lda + kc * 8;  // rows past M load a valid row, never stored
-  }
+    for (int j = 0; j < GA; ++j) {
+      const int r = (wave + NW * j) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(r);
+      pa[j] = A + (size_t)min(m0 + r, M - 1) * lda + kc * 8;  // rows past M load a valid row, never stored
+    }
 #pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    const int r = (wave + NW * j) * 8 + (lane >> 3);
-    const int kc = (lane & 7) ^ swz(r);
-    pb[j] = W + (size_t)(n0 + r) * ldw + kc * 8;
-  }
+    for (int j = 0; j < GB; ++j) {
+      const int r = (wave + NW * j) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(r);
+      pb[j] = W + (size_t)(n0 + r) * ldw + kc * 8;
+    }
+  };
+  aim(lt);
+  auto advance = [&]() {
+    if (++lk == KT) {
+      lk = 0;
+      lt += nblk;
+      if (lt < total) aim(lt);
+    }
+  };
   lds_u16_t* lds = (lds_u16_t*)(lds_void_t*)smem;
 
 
@@ -144,11 +161,11 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
       fa[buf][mi] = *reinterpret_cast<const bf16x8_t*>(&smem[st * STAGE + a_row[mi] + ((kc ^ a_sw[mi]) << 3)]);
     }
   };
-  auto issue_one = [&](int g, int kt, int st) {
+  auto issue_one = [&](int g, int st) {
     if (g < GA)
-      load_lds16(pa[g] + kt * BK, lds + st * STAGE + (wave + NW * g) * 8 * BK);
+      load_lds16(pa[g] + lk * BK, lds + st * STAGE + (wave + NW * g) * 8 * BK);
     else
-      load_lds16(pb[g - GA] + kt * BK, lds + st * STAGE + BM * BK + (wave + NW * (g - GA)) * 8 * BK);
+      load_lds16(pb[g - GA] + lk * BK, lds + st * STAGE + BM * BK + (wave + NW * (g - GA)) * 8 * BK);
   };
   auto mfma_one = [&](int buf, int i) {
     acc[i / NI][i % NI] =
@@ -161,35 +178,94 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   // of the step after; k-step 3 runs half its MFMAs, waits for the next slab
   // and meets the other waves at the barrier, then reads the next slab's
   // first fragments under the other half.
-  auto slab = [&](int kt, auto has_next) {
-    constexpr bool NEXT = decltype(has_next)::value;
-    const int st = kt & 1;
+  // epilogue of the tile at (m0, n0): acc[mi][ni][r] = C[row][col],
+  // row = (r/4)*8 + half*4 + r%4, col = lane%32
+  auto epilogue = [&](int m0, int n0) {
+    if constexpr (EPI == EPI_RESID) {
+      // residual add, one 32-row strip at a time: every load of the strip is in
+      // flight before the first add (rows past M read row M - 1 and are not
+      // stored), so the strip pays one memory latency instead of one per row
+      float* C = reinterpret_cast<float*>(Cv);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        float xv[16][NI];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = min(m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3), M - 1);
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) xv[r][ni] = C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          if (row < M) {
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+              C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)] = xv[r][ni] + acc[mi][ni][r];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          if (row >= M) continue;
+          if constexpr (EPI == EPI_BF16) {
+            uint16_t* C = reinterpret_cast<uint16_t*>(Cv) + (size_t)row * ldc;
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) C[n0 + wn * WTN + ni * 32 + (lane & 31)] = f32_to_bf16(acc[mi][ni][r]);
+          } else {
+            uint16_t* C = reinterpret_cast<uint16_t*>(Cv) + (size_t)row * ldc;
+#pragma unroll
+            for (int ni = 0; ni < NI; ni += 2) {
+              const float g = acc[mi][ni][r], u = acc[mi][ni + 1][r];
+              // silu(g) u with the hardware reciprocal (about 1 ulp; the result
+              // is rounded to bf16)
+              const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+              C[(n0 + wn * WTN + ni * 32) / 2 + (lane & 31)] = f32_to_bf16(h);
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // The last slab of a tile neither waits nor reads ahead: the next tile's
+  // first slab (always issued; past the block's last tile it reloads a slab
+  // of that tile into the free stage) lands under the epilogue.
+  auto slab = [&](int st, auto is_last) {
+    constexpr bool last = decltype(is_last)::value;
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         mfma_one(ks & 1, i);
-        if (ks == 0 && NEXT) {
+        if (ks == 0) {
 #pragma unroll
-          for (int g = i * NG / NM; g < (i + 1) * NG / NM; ++g) issue_one(g, kt + 1, st ^ 1);
+          for (int g = i * NG / NM; g < (i + 1) * NG / NM; ++g) issue_one(g, st ^ 1);
         }
 #pragma unroll
         for (int j = i * NR / NM; j < (i + 1) * NR / NM; ++j) read_one(j, st, ks + 1, (ks + 1) & 1);
         fence();
       }
+      if (ks == 0) advance();
     }
 #pragma unroll
     for (int i = 0; i < NM / 2; ++i) {
       mfma_one(1, i);
       fence();
     }
-    wait_loads();
-    __syncthreads();
+    if constexpr (!last) {
+      wait_loads();
+      __syncthreads();
+    }
     fence();
 #pragma unroll
     for (int i = NM / 2; i < NM; ++i) {
       mfma_one(1, i);
-      if constexpr (NEXT) {
+      if constexpr (!last) {
         const int i2 = i - NM / 2;
 #pragma unroll
         for (int j = i2 * NR / (NM / 2); j < (i2 + 1) * NR / (NM / 2); ++j) read_one(j, st ^ 1, 0, 0);
@@ -198,82 +274,37 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
     }
   };
 
-  const int KT = K / BK;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) issue_one(g, 0, 0);
+  for (int g = 0; g < NG; ++g) issue_one(g, 0);
+  advance();
   wait_loads();
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < NR; ++j) read_one(j, 0, 0, 0);
-  for (int kt = 0; kt + 1 < KT; ++kt) slab(kt, std::true_type{});
-  slab(KT - 1, std::false_type{});
-
-  // epilogue: acc[mi][ni][r] = C[row][col], row = (r/4)*8 + half*4 + r%4, col = lane%32
-  if constexpr (EPI == EPI_RESID) {
-    // residual add, one 32-row strip at a time: every load of the strip is in
-    // flight before the first add (rows past M read row M - 1 and are not
-    // stored), so the strip pays one memory latency instead of one per row
-    float* C = reinterpret_cast<float*>(Cv);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      float xv[16][NI];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = min(m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3), M - 1);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) xv[r][ni] = C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)];
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-        if (row < M) {
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)] = xv[r][ni] + acc[mi][ni][r];
-        }
-      }
+  int st = 0;
+  for (int ct = blockIdx.x;;) {
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+      slab(st, std::false_type{});
+      st ^= 1;
     }
-    return;
+    slab(st, std::true_type{});
+    st ^= 1;
+    epilogue(ct / n_tiles * BM, ct % n_tiles * BN);
+    ct += nblk;
+    if (ct >= total) break;
+    // the next tile's first slab went out under this tile's last slab
+    wait_loads();
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NR; ++j) read_one(j, st, 0, 0);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
   }
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-      if (row >= M) continue;
-      if constexpr (EPI == EPI_BF16) {
-        uint16_t* C = reinterpret_cast<uint16_t*>(Cv) + (size_t)row * ldc;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) C[n0 + wn * WTN + ni * 32 + (lane & 31)] = f32_to_bf16(acc[mi][ni][r]);
-      } else {
-        uint16_t* C = reinterpret_cast<uint16_t*>(Cv) + (size_t)row * ldc;
-#pragma unroll
-        for (int ni = 0; ni < NI; ni += 2) {
-          const float g = acc[mi][ni][r], u = acc[mi][ni + 1][r];
-          // silu(g) u with the hardware reciprocal (about 1 ulp; the result
-          // is rounded to bf16)
-          const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-          C[(n0 + wn * WTN + ni * 32) / 2 + (lane & 31)] = f32_to_bf16(h);
-        }
-      }
-    }
-  }
-}
-
-template <int BM, int BN, int WM, int WN>
-void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W, int ldw,
-                void* C, int ldc, const int32_t* dM, int N, int K) {
-  const int grid = ((cap_m + BM - 1) / BM) * (N / BN);
-  const dim3 blk(WM * WN * 64);
-  if (epi == EPI_BF16)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
-                       ldc, dM, N, K);
-  else if (epi == EPI_RESID)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_RESID>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
-                       ldc, dM, N, K);
-  else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_SWIGLU>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
-                       ldc, dM, N, K);
+  wait_loads();  // no load into LDS outlives the workgroup
 }
 
 int cu_count() {
@@ -286,6 +317,26 @@ int cu_count() {
   }();
   return n;
 }
+
+template <int BM, int BN, int WM, int WN>
+void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W, int ldw,
+                void* C, int ldc, const int32_t* dM, int N, int K) {
+  // persistent workgroups: one per tile up to one per CU (a two-lane split
+  // still gives each launch the whole chip: capping it at its share of the
+  // CUs measured 6% slower per call)
+  const int grid = std::min(((cap_m + BM - 1) / BM) * (N / BN), cu_count());
+  const dim3 blk(WM * WN * 64);
+  if (epi == EPI_BF16)
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+                       ldc, dM, N, K);
+  else if (epi == EPI_RESID)
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_RESID>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+                       ldc, dM, N, K);
+  else
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_SWIGLU>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+                       ldc, dM, N, K);
+}
+
 
 }  // namespace
 
