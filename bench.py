@@ -513,16 +513,16 @@ def summarize_traffic(out_dir, warmup, steps, pool_size):
     print(json.dumps(out), flush=True)
 
 
-def summarize_trace(trace_dir, steps, C):
+def summarize_trace(trace_dir, warmup, steps):
     """Per-kernel summary of a rocprofv3 --kernel-trace run of the headline
     bench (markdown rows on stdout): dispatches, average duration, the union of
     the dispatch intervals (device time the kernel ran, counting concurrent
     dispatches once), and the average over dispatches that ran alone (no other
-    dispatch overlapping them).  Then the gate/up GEMM by launch size, and its
-    average over the one-lane timed region alone, the launches the bench's HIP
-    events time: a one-launch call ends with a gate/up launch over its C x 100
-    branch rows, and the bench runs `steps` such calls to prime the graphs,
-    then the `steps` timed ones."""
+    dispatch overlapping them).  Then the gate/up GEMM's average over the
+    one-lane timed region alone, the launches the bench's HIP events time.
+    Every forward starts with one gather (k_embed); the bench runs warmup +
+    2 x steps two-lane calls (two forwards each), then `steps` one-lane calls
+    to prime the graphs, then the `steps` timed one-lane calls."""
     import csv
     rows = []
     for root, _, files in os.walk(trace_dir):
@@ -531,11 +531,6 @@ def summarize_trace(trace_dir, steps, C):
                 with open(os.path.join(root, fn)) as f:
                     rows += list(csv.DictReader(f))
     ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
-    grids = {}
-    for r in rows:  # the gate/up GEMM by launch size (grid blocks)
-        if "k_gemm<256, 256, 4, 2, 2>" in r["Kernel_Name"]:
-            blocks = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
-            grids.setdefault(blocks, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     alone = []
     hi = -1  # latest end among earlier dispatches
     for i, (a, b, _) in enumerate(ev):
@@ -572,19 +567,15 @@ def summarize_trace(trace_dir, steps, C):
         solo_txt = f"{len(solo)}, {sum(solo) / len(solo) / 1e3:.1f}" if solo else "0, -"
         print(f"| `{name}` | {st['n']} | {st['sum'] / st['n'] / 1e3:.1f} | {u / 1e6:.2f} | {solo_txt} | "
               f"{st['sum'] / total * 100:.1f} |")
-    print()
-    print("| gate/up GEMM launch size (blocks) | dispatches | avg us |")
-    print("|---|---|---|")
-    for blocks, d in sorted(grids.items(), key=lambda kv: -kv[0]):
-        print(f"| {blocks} | {len(d)} | {sum(d) / len(d) / 1e3:.1f} |")
-    gu = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
-                 int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+    fwd = sorted(int(r["Start_Timestamp"]) for r in rows if "k_embed" in r["Kernel_Name"])
+    gu = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
                 for r in rows if "k_gemm<256, 256, 4, 2, 2>" in r["Kernel_Name"])
-    tail_blocks = -(-C * 100 // 256) * (2 * 3072 // 256)  # 256 x 256 tiles over the branch rows
-    tails = [i for i, g in enumerate(gu) if g[2] == tail_blocks]
-    if len(tails) >= 2 * steps:
-        win = gu[tails[steps - 1] + 1:tails[2 * steps - 1] + 1]
-        avg = sum(b - a for a, b, _ in win) / len(win) / 1e3
+    first = 2 * (warmup + 2 * steps) + steps  # the first timed one-lane forward
+    if len(fwd) >= first + steps:
+        t0 = fwd[first]
+        t1 = fwd[first + steps] if len(fwd) > first + steps else float("inf")
+        win = [(a, b) for a, b in gu if t0 <= a < t1]
+        avg = sum(b - a for a, b in win) / max(len(win), 1) / 1e3
         print()
         print(f"one-lane timed region: {len(win)} gate/up dispatches ({steps} calls), avg {avg:.1f} us")
 
@@ -630,7 +621,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.steps, args.concurrency)
+        summarize_trace(args.summarize_trace, args.warmup, args.steps)
         return
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic, args.warmup, args.steps, args.pool)
