@@ -75,6 +75,58 @@ def test_gemm(M, N, K, epi):
         assert np.all(np.abs(got - want) <= tol)
 
 
+@pytest.mark.parametrize("M,N,K,epi", [(30011, 6144, 1024, "swiglu"), (30011, 4096, 1024, "bf16"),
+                                        (30011, 1024, 3072, "resid")])
+def test_gemm_many_tiles_sampled(M, N, K, epi):
+    # Workgroups walk many tiles each (one workgroup per CU), with a ragged last
+    # row tile; rows sampled across the range, including the last one, against
+    # float64 products of the same bf16 operands.
+    rng = np.random.default_rng(M + N + K)
+    a_bits, a = bf16_tensor(rng, (M, K))
+    w_bits, w = bf16_tensor(rng, (N, K), 0.05)
+    rows = np.unique(np.concatenate([rng.integers(0, M, 40), np.arange(M - 24, M), [0, 255, 256]]))
+    ref = a[rows] @ w.T
+    bound = np.abs(a[rows]) @ np.abs(w).T * (K * 2.0 ** -23)
+    dA = to_dev(a_bits.view(np.int16))
+    if epi == "bf16":
+        dW = to_dev(w_bits.view(np.int16))
+        dC = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+        spa.duolm_debug_gemm(0, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K)
+        got = widen_bf16(dC.cpu().numpy().view(np.uint16)[rows])
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + bound + 1e-30)
+    elif epi == "resid":
+        dW = to_dev(w_bits.view(np.int16))
+        c0 = rng.standard_normal((M, N)).astype(np.float32)
+        dC = to_dev(c0)
+        spa.duolm_debug_gemm(1, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K)
+        got = dC.cpu().numpy()[rows].astype(np.float64)
+        want = c0[rows].astype(np.float64) + ref
+        assert np.all(np.abs(got - want) <= bound + np.abs(want) * 2.0 ** -23 + 1e-30)
+    else:
+        F = N // 2
+        inter = np.empty_like(w_bits)
+        for p in range(F // 32):
+            inter[64 * p:64 * p + 32] = w_bits[32 * p:32 * p + 32]
+            inter[64 * p + 32:64 * p + 64] = w_bits[F + 32 * p:F + 32 * p + 32]
+        dW = to_dev(inter.view(np.int16))
+        dC = torch.zeros((M, F), dtype=torch.int16, device="cuda")
+        spa.duolm_debug_gemm(2, dA.data_ptr(), dW.data_ptr(), dC.data_ptr(), M, N, K)
+        got = widen_bf16(dC.cpu().numpy().view(np.uint16)[rows])
+        g, u = ref[:, :F], ref[:, F:]
+        want = g / (1 + np.exp(-g)) * u
+        tol = np.abs(want) * 2.0 ** -8 + (np.abs(u) * 1.2 + np.abs(g)) * bound[:, :F] * 2 + 1e-30
+        assert np.all(np.abs(got - want) <= tol)
+    # rows are batch invariant: a launch over a slice reproduces them bit for bit
+    lo = int(rows[len(rows) // 2])
+    n = 300
+    sub = torch.zeros((n, dC.shape[1]), dtype=dC.dtype, device="cuda")
+    if epi == "resid":
+        sub.copy_(to_dev(c0[lo:lo + n]))
+    spa.duolm_debug_gemm({"bf16": 0, "resid": 1, "swiglu": 2}[epi], dA[lo:lo + n].data_ptr(), dW.data_ptr(),
+                         sub.data_ptr(), n, N, K)
+    assert torch.equal(sub, dC[lo:lo + n])
+
+
 def test_copy_kernel():
     x = torch.randint(-2 ** 31, 2 ** 31 - 1, (1 << 20,), dtype=torch.int32, device="cuda")
     y = torch.zeros_like(x)
