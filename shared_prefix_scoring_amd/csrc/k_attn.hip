@@ -42,9 +42,15 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-// 16 bytes per lane, global -> LDS; lane i lands at lds + 16 i
+// 16 bytes per lane, global -> LDS; lane i lands at lds + 16 i.  M0 holds the
+// wave's LDS destination; one wait state separates the M0 write from the load
+// that reads it.  Written as inline asm so that the compiler does not count
+// it against the LDS reads (it would then make every fragment read wait for
+// all LDS traffic); the kernel waits for it with s_waitcnt vmcnt before the
+// barrier that publishes the tile.
 __device__ __forceinline__ void load_lds16(const uint16_t* g, lds_u16_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+  const uint32_t base = (uint32_t)(uintptr_t)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(base) : "memory");
 }
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Within each 16-lane group, lane i gets element i % 4 of the 8-byte reads of
@@ -265,6 +271,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   auto tile = [&](int t, auto st) {
     constexpr int ST = decltype(st)::value;
     const int k0 = t * BKV;
+    // the next tile's K and V (and, on the first tile, the rows' own K and V)
+    // go out first: the other stage was released at the last barrier, so the
+    // loads have the whole tile to land
+    if (t + 1 < ntiles) issue(k0 + BKV, std::integral_constant<int, ST ^ 1>{});
+    if (t == 0) issue_own();
     const uint16_t* const Kt = kt(st);
     const lds_u16_t* const vb = (const lds_u16_t*)(lds_void_t*)vt(st);
     const bool busy = wave_active && k0 <= wave_klim;
@@ -291,14 +302,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
       for (int kb = 0; kb < KB; ++kb) n[kb] = ks + 1 < NKS ? kfrag(kb, ks + 1) : a[kb];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], qf[ks], s[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // the reads stay one k-step ahead of their MFMAs
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) a[kb] = n[kb];
     }
     }  // QK of this tile
-    // the next tile's K and V (and, on the first tile, the rows' own K and V)
-    // go out while the QK products drain
-    if (t + 1 < ntiles) issue(k0 + BKV, std::integral_constant<int, ST ^ 1>{});
-    if (t == 0) issue_own();
     if (busy) {
     // tile max of the raw scores (masked keys -> -inf); the mask is only
     // evaluated on tiles that reach past some column's last visible key
