@@ -321,10 +321,13 @@ int cu_count() {
 template <int BM, int BN, int WM, int WN>
 void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W, int ldw,
                 void* C, int ldc, const int32_t* dM, int N, int K) {
-  // persistent workgroups: one per tile up to one per CU (a two-lane split
-  // still gives each launch the whole chip: capping it at its share of the
-  // CUs measured 6% slower per call)
-  const int grid = std::min(((cap_m + BM - 1) / BM) * (N / BN), cu_count());
+  // Persistent workgroups for the large tiles, whose LDS stages (112-128 KB)
+  // allow one workgroup per CU: one per tile up to one per CU (a two-lane
+  // split still gives each launch the whole chip: capping it at its share of
+  // the CUs measured 6% slower per call).  Smaller tiles fit several
+  // workgroups per CU, so they get one workgroup per tile.
+  const int tiles = ((cap_m + BM - 1) / BM) * (N / BN);
+  const int grid = 2 * (BM + BN) * BK * 2 > 96 * 1024 ? std::min(tiles, cu_count()) : tiles;
   const dim3 blk(WM * WN * 64);
   if (epi == EPI_BF16)
     hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
