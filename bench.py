@@ -130,8 +130,8 @@ def bench_packer(ranker, cfg):
     out["pack_10k_one_call_8thr_ms"] = round(dt * 1e3, 2)
     stream = torch.cuda.current_stream().cuda_stream
     calls = 20
-    for s in range(0, 64 * 3, 64):  # warm the shape buckets
-        ids, L, K, M = spa.duolm_pack_requests(pack, ids=buf, start=s, count=64)
+    for c in range(calls):  # capture every shape bucket the timed calls use
+        ids, L, K, M = spa.duolm_pack_requests(pack, ids=buf, start=64 * c, count=64)
         ranker.score_packed(L, K, M, ids, stream=stream)
     t0 = time.perf_counter()
     for c in range(calls):
@@ -782,10 +782,14 @@ def main():
         log("open-loop Poisson run")
         req_rate = value / 100.0 * 0.9
         pack = pack_pool(pool, 3, cfg)
-        # prime the graphs of the batch sizes the open loop will produce
+        # prime the graphs of the batch sizes the open loop will produce, then
+        # warm the graph cache as a serving process would be: an untimed open
+        # loop of the same rate with other arrivals (another seed), whose
+        # batches fall in the shape buckets the timed run mostly meets
         for c in range(1, C + 1):
             ids, L, K, M = spa.duolm_pack_requests(pack, count=c)
             ranker.score_packed(L, K, M, ids, use_graph=use_graph, stream=stream)
+        open_loop(ranker, pack, req_rate, args.open_loop // 2, seed=7, C=C, use_graph=use_graph, stream=stream)
         ol_lat, ol_wall = open_loop(ranker, pack, req_rate, args.open_loop, seed=103, C=C,
                                     use_graph=use_graph, stream=stream)
         out["p99_ms"] = round(float(np.percentile(ol_lat, 99)), 3)
@@ -795,7 +799,8 @@ def main():
                             "p99_ms": out["p99_ms"],
                             "scores_per_s": round(args.open_loop * 100 / ol_wall, 1),
                             "path": "structured requests -> host packer -> page-locked staging -> "
-                                    "scores to host (PCIe-inclusive)"}
+                                    "scores to host (PCIe-inclusive)",
+                            "warmup": "an untimed open loop of half as many requests, other arrivals"}
     if args.breakdown:
         ranker.set_profiling(spa.KERNEL_CLASSES)
         for i in range(min(5, len(batches))):
