@@ -47,7 +47,10 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 // that reads it.  Written as inline asm so that the compiler does not count
 // it against the LDS reads (it would then make every fragment read wait for
 // all LDS traffic); the kernel waits for it with s_waitcnt vmcnt before the
-// barrier that publishes the tile.
+// barrier that publishes the tile.  The instruction has no register
+// result (its data goes to LDS), so no register the compiler reallocates can
+// be written by it while it is in flight; its address VGPRs and M0 are read
+// when it issues, as with the builtin form of the same load.
 __device__ __forceinline__ void load_lds16(const uint16_t* g, lds_u16_t* lds) {
   const uint32_t base = (uint32_t)(uintptr_t)lds;
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(base) : "memory");

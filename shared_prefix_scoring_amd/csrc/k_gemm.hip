@@ -53,7 +53,10 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 // 16 bytes per lane, global -> LDS; lane i lands at lds + 16 i.  M0 holds the
 // wave's LDS destination; one wait state separates the M0 write from the load
 // that reads it.  Nothing is returned to registers: the caller waits with
-// s_waitcnt vmcnt before the barrier that publishes the stage.
+// s_waitcnt vmcnt before the barrier that publishes the stage.  The instruction has no register
+// result (its data goes to LDS), so no register the compiler reallocates can
+// be written by it while it is in flight; its address VGPRs and M0 are read
+// when it issues, as with the builtin form of the same load.
 __device__ __forceinline__ void load_lds16(const uint16_t* g, lds_u16_t* lds) {
   const uint32_t base = (uint32_t)(uintptr_t)lds;
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(base) : "memory");
