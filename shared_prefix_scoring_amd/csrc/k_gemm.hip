@@ -185,26 +185,29 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   // row = (r/4)*8 + half*4 + r%4, col = lane%32
   auto epilogue = [&](int m0, int n0) {
     if constexpr (EPI == EPI_RESID) {
-      // residual add, one 32-row strip at a time: every load of the strip is in
-      // flight before the first add (rows past M read row M - 1 and are not
-      // stored), so the strip pays one memory latency instead of one per row
+      // residual add, 8 of a lane's rows at a time: every load of the group is
+      // in flight before the first add (rows past M read row M - 1 and are not
+      // stored), so a group pays one memory latency instead of one per row
       float* C = reinterpret_cast<float*>(Cv);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        float xv[16][NI];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = min(m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3), M - 1);
+        for (int r0 = 0; r0 < 16; r0 += 8) {
+          float xv[8][NI];
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni) xv[r][ni] = C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)];
-        }
+          for (int r = 0; r < 8; ++r) {
+            const int row = min(m0 + wm * WTM + mi * 32 + ((r0 + r) >> 2) * 8 + half * 4 + (r & 3), M - 1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * WTM + mi * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          if (row < M) {
+            for (int ni = 0; ni < NI; ++ni) xv[r][ni] = C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)];
+          }
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-              C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)] = xv[r][ni] + acc[mi][ni][r];
+          for (int r = 0; r < 8; ++r) {
+            const int row = m0 + wm * WTM + mi * 32 + ((r0 + r) >> 2) * 8 + half * 4 + (r & 3);
+            if (row < M) {
+#pragma unroll
+              for (int ni = 0; ni < NI; ++ni)
+                C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)] = xv[r][ni] + acc[mi][ni][r0 + r];
+            }
           }
         }
       }
