@@ -156,7 +156,11 @@ static bool launch_export_dt(hipStream_t s, const void* a, int64_t n_rows, int d
   EXPORT_CASE(4)
   EXPORT_CASE(8)
   EXPORT_CASE(16)
-  EXPORT_CASE(32)
+  // 32 chunks per lane only where the widest row needs them (fp32 input):
+  // 2-byte inputs reach kMaxExportDim at 16
+  if constexpr (Chunk<DT>::N * 64 * 16 < kMaxExportDim) {
+    EXPORT_CASE(32)
+  }
 #undef EXPORT_CASE
   return false;
 }
