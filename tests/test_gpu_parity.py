@@ -120,6 +120,26 @@ def test_stress_shape_sampled(gpu_qwen):
     np.testing.assert_array_equal(r.score([(p, c[pick])]), mis[pick])
 
 
+def test_longest_prefix(gpu_qwen):
+    # The longest accepted prefix puts its candidates at the rotary table's
+    # last position: MIS against independent scoring there, and one more row
+    # is refused before anything runs.
+    cfg, _, _, _, r = gpu_qwen
+    lmax = r.dims.max_prefix
+    (p, c), = reqs_of(cfg, 5, n=1)
+    prefix = np.resize(p, lmax).astype(np.int32)  # the L = 4096 request's ids, repeated
+    cands = c[[0, 255, 511]]
+    mis = r.score([(prefix, cands)])
+    assert np.all(np.isfinite(mis))
+    ind = r.score([(prefix, cands)], mode=IND)
+    e = score_err(mis, ind)
+    print(f"L = {lmax}: MIS vs independent {e:.3e}")
+    assert e <= MIS_VS_IND_TOL
+    with pytest.raises(spa.DuolmError) as ei:
+        r.score([(np.resize(p, lmax + 1).astype(np.int32), cands)])
+    assert ei.value.status == "EINVAL"
+
+
 def test_graph_matches_eager_and_repeats(gpu_qwen):
     cfg, _, _, _, r = gpu_qwen
     reqs = reqs_of(cfg, 3, n=12)
