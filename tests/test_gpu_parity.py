@@ -140,6 +140,27 @@ def test_longest_prefix(gpu_qwen):
     assert ei.value.status == "EINVAL"
 
 
+def test_launch_row_limit_splits_calls(gpu_qwen, monkeypatch):
+    # A ranker whose launches hold at most 4096 rows scores a 64-request batch
+    # (about 21k rows) as several launches, request by request, with the same
+    # bits as one launch; a single request over the limit is refused.
+    cfg, w, D, _, r = gpu_qwen
+    monkeypatch.setenv("DUOLM_MAX_ROWS", "4096")
+    small = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
+    try:
+        assert small.dims.max_rows == 4096
+        small.load_vid_table(D)
+        reqs = reqs_of(cfg, 3, n=64)
+        assert sum(len(p) + len(c) for p, c in reqs) > 4 * 4096
+        np.testing.assert_array_equal(small.score(reqs), r.score(reqs))
+        (p, c), = reqs_of(cfg, 5, n=1)  # 4096 + 512 rows
+        with pytest.raises(spa.DuolmError) as ei:
+            small.score([(p, c)])
+        assert ei.value.status == "EINVAL"
+    finally:
+        small.close()
+
+
 def test_graph_matches_eager_and_repeats(gpu_qwen):
     cfg, _, _, _, r = gpu_qwen
     reqs = reqs_of(cfg, 3, n=12)
