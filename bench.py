@@ -628,7 +628,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU scaling is not implemented "
+        print(json.dumps({"error": "the ranker runs on one GPU only; multi-GPU scaling is not implemented "
                                    "(requests are independent, so the path would shard by request)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
