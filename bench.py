@@ -430,6 +430,29 @@ def bench_session(ranker, cfg, steps):
     return out
 
 
+def summarize_counters(out_dir):
+    """Average of every counter of a rocprofv3 --pmc run (all counter_collection
+    csv files under out_dir) per kernel template, as markdown rows."""
+    import csv
+    acc = {}
+    for root, _, files in os.walk(out_dir):
+        for fn in files:
+            if not fn.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(root, fn)) as f:
+                for r in csv.DictReader(f):
+                    n = r["Kernel_Name"]
+                    n = n.replace("duolm::", "").replace("(anonymous namespace)::", "").replace("void ", "")
+                    n = n[:n.index("(")] if "(" in n else n
+                    acc.setdefault(n, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    counters = sorted({c for v in acc.values() for c in v})
+    print("| kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|" + "---|" * len(counters))
+    for n, v in sorted(acc.items()):
+        cells = [f"{sum(v[c]) / len(v[c]):.4g}" if c in v else "-" for c in counters]
+        print(f"| `{n}` | {len(next(iter(v.values())))} | " + " | ".join(cells) + " |")
+
+
 def summarize_traffic(out_dir, warmup, steps, pool_size):
     """Turn the four counter passes (FETCH_SIZE and WRITE_SIZE of the gate/up
     GEMM in an eager `--no-graph --max-lanes 1 --open-loop 0 --cpu-baseline-s 0` run with the
@@ -608,6 +631,8 @@ def main():
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print a per-kernel summary of a rocprofv3 --kernel-trace run under DIR (no GPU)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print per-kernel averages of a rocprofv3 --pmc run under DIR (no GPU)")
     ap.add_argument("--summarize-traffic", metavar="DIR",
                     help="write profiles/traffic_gemm_gateup.json from the counter runs under DIR (no GPU)")
     ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export", "packer", "session"],
@@ -620,6 +645,9 @@ def main():
                          "prefix recompute")
     args = ap.parse_args()
 
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.warmup, args.steps)
         return
