@@ -332,9 +332,10 @@ def _mv_check(model, reqs, m, got):
     return per
 
 
-@pytest.mark.parametrize("m,n_cand", [(2, 8), (3, 50)])
+@pytest.mark.parametrize("m,n_cand", [(2, 8), (3, 50), (64, 3)])
 def test_multivector_tiny(gpu_tiny, m, n_cand):
-    # m = 3 with 50 candidates: 150 branch rows, tiles of 42 whole branches
+    # m = 3 with 50 candidates: 150 branch rows, tiles of 42 whole branches;
+    # m = 64, the longest candidate accepted: two whole branches fill a tile
     cfg, _, _, model, r = gpu_tiny
     reqs = [(q.prefix, q.cands) for q in synth.make_requests(1, cfg, m=m, n_cand=n_cand)]
     for g in (False, True):
