@@ -79,6 +79,26 @@ def test_batched_sessions_across_pages(gpu_qwen, cid, n):
             x.close()
 
 
+def test_page_aligned_appends(gpu_tiny):
+    # appends that end exactly on 64-row page boundaries, then one row into a
+    # fresh page; every step's scores equal one-call scoring of the prefix so far
+    cfg, _, _, _, r = gpu_tiny
+    r.kv_pool_init(64 * 16)
+    q = synth.make_requests(1, cfg)[0]
+    prefix = np.resize(q.prefix, 129).astype(np.int32)
+    s = r.session()
+    try:
+        done = 0
+        for part in chunks(prefix, [64, 128]):  # 64, 64 and 1 rows
+            got = r.step([s], [part], [q.cands])
+            done += len(part)
+            assert s.length == done
+            np.testing.assert_array_equal(got, r.score([(prefix[:done], q.cands)]))
+        assert r.kv_free_pages() == 16 - 3
+    finally:
+        s.close()
+
+
 def test_mixed_step_and_pool_accounting(gpu_tiny):
     cfg, _, _, model, r = gpu_tiny
     r.kv_pool_init(10 * 64)
