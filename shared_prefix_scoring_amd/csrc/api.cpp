@@ -61,26 +61,9 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int64_t kDefaultMaxRows = 262144;
 
-// Launch prefix and branch attention tiles together (build with
-// -DDUOLM_MERGED_ATTN=0 for two launches per layer).
-#ifndef DUOLM_MERGED_ATTN
-#define DUOLM_MERGED_ATTN 1
-#endif
-constexpr bool kMergedAttn = DUOLM_MERGED_ATTN != 0;
-
 // Calls of at least this many rows (and two sequences) run as two halves
 // side by side, one per execution lane.
-#ifndef DUOLM_LANE_MIN_ROWS
-#define DUOLM_LANE_MIN_ROWS 2048
-#endif
-constexpr int64_t kLaneMinRows = DUOLM_LANE_MIN_ROWS;
-
-// Run the last layer past its QKV projection over the branch rows only
-// (build with -DDUOLM_BRANCH_ONLY_TAIL=0 to compute every row there).
-#ifndef DUOLM_BRANCH_ONLY_TAIL
-#define DUOLM_BRANCH_ONLY_TAIL 1
-#endif
-constexpr bool kBranchOnlyTail = DUOLM_BRANCH_ONLY_TAIL != 0;
+constexpr int64_t kLaneMinRows = 2048;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -158,10 +141,7 @@ struct GraphEntry {
 // round of its GEMMs leave CUs idle that the other half's kernels fill (a
 // 64-request batch as two concurrent halves took 26.1 ms against 28.3 ms as
 // one launch, measured with two handles).
-#ifndef DUOLM_LANES
-#define DUOLM_LANES 2
-#endif
-constexpr int kLanes = DUOLM_LANES;
+constexpr int kLanes = 2;
 struct Lane {
   hipStream_t stream = nullptr;  // lane 1: its own stream; lane 0 runs on the call's stream
   hipEvent_t done = nullptr;     // lane 1 finished the call's launches
@@ -786,7 +766,7 @@ void enqueue_forward(Enq& q, const Caps& c) {
     // branch tiles): after its QKV projection it runs over the branch rows
     // [0, n_brows) only -- no prefix attention, O projection, MLP.  A debug
     // stop reads whole layers, so it keeps every row.
-    const bool tail = kBranchOnlyTail && l == D.n_layers - 1 && q.stop_layer < 0;
+    const bool tail = l == D.n_layers - 1 && q.stop_layer < 0;
     q.brows = false;
     q.run(DUOLM_K_RMSNORM, [&] { launch_rmsnorm(s, c.T, ln->X, W.attn_norm, ln->Xn, dT, d, eps); });
     if (q.stop(l, DUOLM_STAGE_ATTN_NORM)) return;
@@ -800,8 +780,7 @@ void enqueue_forward(Enq& q, const Caps& c) {
     if (c.session) launch_kv_store(s, c.T, ln->QKV, nq, bl, H, Hk, hd);
     // prefix and branch tiles in one launch, side by side on the chip; apart
     // when either kind is being timed
-    const bool split = !kMergedAttn || ((R->prof_mask >> DUOLM_K_ATTN_PREFIX) & 1u) ||
-                       ((R->prof_mask >> DUOLM_K_ATTN_BRANCH) & 1u);
+    const bool split = ((R->prof_mask >> DUOLM_K_ATTN_PREFIX) & 1u) || ((R->prof_mask >> DUOLM_K_ATTN_BRANCH) & 1u);
     if (tail) {
       if (c.bitems > 0)
         q.run(DUOLM_K_ATTN_BRANCH,

@@ -30,13 +30,6 @@ namespace duolm {
 
 namespace {
 
-#ifndef ATTN_NW
-#define ATTN_NW 8
-#endif
-#ifndef ATTN_BKV
-#define ATTN_BKV 64
-#endif
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -468,8 +461,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   }
 }
 
-constexpr int NW = ATTN_NW;    // query columns per workgroup = 32 NW
-constexpr int BKV = ATTN_BKV;  // keys per streamed tile
+constexpr int NW = 8;    // query columns per workgroup = 32 NW
+constexpr int BKV = 64;  // keys per streamed tile
 
 template <int HD>
 void launch_hd(hipStream_t s, int cap_p, int cap_b, const uint16_t* QKV, int ld, uint16_t* O, int ldo,

@@ -12,9 +12,49 @@ import pytest
 import torch
 import torch.nn.functional as F
 
-from oracle import attention, layer_stages, mlp_swiglu, rmsnorm, rope_rotate, score_head
+from oracle import attention, layer_stages, mlp_swiglu, rmsnorm, rope_rotate, score_head, widen_bf16, widen_f16
 
 RNG = np.random.default_rng(1234)
+
+
+# ------------------------------------------------------- storage widening ---
+
+
+def _special_bits():
+    # zeros, smallest and largest subnormals and normals, one, infinities, a NaN,
+    # then every pattern of a random draw
+    fixed = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F, 0x3F80, 0xBF80,
+             0x7F80, 0xFF80, 0x7FC0, 0x03FF, 0x0400, 0x7BFF, 0x3C00, 0x7C00, 0xFC00, 0x7E00]
+    return np.concatenate([np.array(fixed, np.uint16), RNG.integers(0, 1 << 16, 4096).astype(np.uint16)])
+
+
+def _same_values(got, ref):
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_widen_bf16_matches_torch():
+    # torch's own bfloat16 -> float64 conversion of the same bit patterns
+    bits = _special_bits()
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = widen_bf16(bits)
+    assert got.dtype == np.float64
+    _same_values(got, ref)
+    # hand values: 1.0, -2.0, the largest finite bf16 and the smallest subnormal
+    assert widen_bf16(np.array([0x3F80, 0xC000, 0x7F7F, 0x0001], np.uint16)).tolist() == [
+        1.0, -2.0, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133]
+
+
+def test_widen_f16_matches_torch():
+    bits = _special_bits()
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.float16).to(torch.float64).numpy()
+    got = widen_f16(bits)
+    assert got.dtype == np.float64
+    _same_values(got, ref)
+    assert widen_f16(np.array([0x3C00, 0xC000, 0x7BFF, 0x0001], np.uint16)).tolist() == [
+        1.0, -2.0, 65504.0, 2.0 ** -24]
 
 
 # ---------------------------------------------------------------- RMSNorm ---
