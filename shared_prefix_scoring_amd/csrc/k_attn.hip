@@ -92,21 +92,20 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   constexpr int KB = BKV / 32;         // 32-key blocks per tile
   static_assert(BKV == 32 || BKV == 64, "key tile");
   static_assert(kPageRows % BKV == 0, "a key tile lies in one session page");
-  constexpr int QCH = NC * CPR;        // 16-byte chunks of the query block
+  constexpr int QCH = NC * CPR;        // 16-byte chunks of the query / output block
   static_assert(QCH % (64 * NW) == 0, "staging layout");
   auto vswz = [](int key) { return vswz_t<CPR>(key); };
   auto cswz = [](int c) { return c & (CPR - 1); };  // chunk swizzle of a query column / own-key row
-  // LDS: K and V tiles per pipeline stage, and the query block.  The query
-  // block is copied to registers first, then holds the rows' own K and V,
-  // and finally stages the output.  Each stage is an array of its own, so the
-  // compiler can see that reads of one stage never touch the global->LDS
-  // copies in flight into the other (one array indexed by a runtime stage
-  // made it wait for those copies before every V read).
+  // LDS: K and V tiles per pipeline stage, and the own-key block, which holds
+  // the rows' own K and V and finally stages the output.  Each stage is an
+  // array of its own, so the compiler can see that reads of one stage never
+  // touch the global->LDS copies in flight into the other (one array indexed
+  // by a runtime stage made it wait for those copies before every V read).
   __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t Qs[NC * HD];
+  __shared__ __attribute__((aligned(1024))) uint16_t Own[NC * HD];
 
   // the item and the item count load together (the grid never exceeds the
   // item buffer, so the read is in bounds even for surplus blocks; testing
@@ -172,27 +171,23 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   // packed rows: query row i of the item (and its own K/V) at qrow0 + i, prefix
   // key k at koff + k (offsets are virtual, so only these sums are addresses)
   const int qrow0 = sd.row_off + item_row0;
-  lds_u16_t* const ldsQ = (lds_u16_t*)(lds_void_t*)Qs;
+  lds_u16_t* const ldsOwn = (lds_u16_t*)(lds_void_t*)Own;
   // stage ST's K and V tiles
   auto kt = [&](auto st) -> uint16_t* { if constexpr (decltype(st)::value == 0) return sK0; else return sK1; };
   auto vt = [&](auto st) -> uint16_t* { if constexpr (decltype(st)::value == 0) return sV0; else return sV1; };
 
-  // Query block: column c = (row c / G, head c % G of this KV head's group);
-  // its HD values are one run of 16-byte chunks, chunk k stored at slot
-  // k ^ (c % CPR).  Rows of the G heads are contiguous in memory, so each
-  // load instruction reads whole rows.  Rows past the item's last load the
-  // last row (valid memory, never stored).
+  // Query fragments straight from memory into registers: lane (column qc,
+  // half h) holds chunks 2 ks + h (ks = 0 .. NKS-1) of its query, the B
+  // operand of S^T = K Q^T.  Columns past the item's last row load the last
+  // row (valid memory, never stored).
+  bf16x8_t qf[NKS];
+  {
+    const uint16_t* qsrc =
+        QKV + (size_t)(qrow0 + min(lrow, item_nrows - 1)) * ld + (g * G + qc % G) * HD + half * 8;
 #pragma unroll
-  for (int j = 0; j < QCH / (64 * NW); ++j) {
-    const int c = (wave + j * NW) * 64 + lane;
-    const int col = c / CPR, slot = c % CPR;
-    const int lr = min(col / G, item_nrows - 1);
-    const uint16_t* src =
-        QKV + (size_t)(qrow0 + lr) * ld + (g * G + col % G) * HD + ((slot ^ cswz(col)) << 3);
-    load_lds16(src, ldsQ + (c - lane) * 8);
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qsrc + ks * 16);
   }
 
-  bf16x8_t qf[NKS];
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -239,19 +234,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
-  const int ntiles = (kend + BKV - 1) / BKV;
-  if (ntiles > 0) issue(0, S0{});
-  wait_loads();
-  __syncthreads();
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8_t*>(&Qs[qc * HD + (((ks * 2 + half) ^ cswz(qc)) << 3)]);
-  __syncthreads();  // every wave holds its query fragments; the block is free
-
-  // The rows' own K and V into the query block: own-K row r at [r HD], own-V
-  // row r at [(rows_per_item + r) HD], chunk k at slot k ^ (r % CPR).  Issued
-  // once the first key tile's QK product is under way, so they fly while that
-  // tile is finished.
+  // The rows' own K and V into the own-key block: own-K row r at [r HD],
+  // own-V row r at [(rows_per_item + r) HD], chunk k at slot k ^ (r % CPR).
   auto issue_own = [&]() {
     const int sin = QCH / (64 * G);  // load instructions per matrix
     for (int ins = wave; ins < 2 * sin; ins += NW) {
@@ -260,18 +244,24 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
       const int r = c / CPR, slot = c % CPR;
       const int lr = min(r, item_nrows - 1);
       const uint16_t* src = QKV + (size_t)(qrow0 + lr) * ld + (isv ? vcol : kcol) + ((slot ^ cswz(r)) << 3);
-      load_lds16(src, ldsQ + (isv ? rows_per_item * HD : 0) + (c - lane) * 8);
+      load_lds16(src, ldsOwn + (isv ? rows_per_item * HD : 0) + (c - lane) * 8);
     }
   };
+
+  // Everything the item reads before its first tile goes out at once: the
+  // query fragments (above), the first key tile and the rows' own K and V.
+  const int ntiles = (kend + BKV - 1) / BKV;
+  if (ntiles > 0) issue(0, S0{});
+  issue_own();
+  wait_loads();
+  __syncthreads();
 
   auto tile = [&](int t, auto st) {
     constexpr int ST = decltype(st)::value;
     const int k0 = t * BKV;
-    // the next tile's K and V (and, on the first tile, the rows' own K and V)
-    // go out first: the other stage was released at the last barrier, so the
-    // loads have the whole tile to land
+    // the next tile's K and V go out first: the other stage was released at
+    // the last barrier, so the loads have the whole tile to land
     if (t + 1 < ntiles) issue(k0 + BKV, std::integral_constant<int, ST ^ 1>{});
-    if (t == 0) issue_own();
     const uint16_t* const Kt = kt(st);
     const lds_u16_t* const vb = (const lds_u16_t*)(lds_void_t*)vt(st);
     const bool busy = wave_active && k0 <= wave_klim;
@@ -378,9 +368,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     tile(t, S0{});
     if (t + 1 < ntiles) tile(t + 1, S1{});
   }
-  if (ntiles == 0) issue_own();
-  wait_loads();
-  __syncthreads();
+  // (every load has landed and been published: at the start, or at the end
+  // of the last tile)
 
   if (wave_active) {
     // The row's own key and, in a candidate branch, the earlier rows of its
@@ -392,7 +381,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     for (int e = 0; e < M; ++e) {
       const bool act = e < nmerge;
       const int kr = act ? lrow - nmerge + 1 + e : lrow;
-      const uint16_t* kself = Qs + kr * HD;
+      const uint16_t* kself = Own + kr * HD;
       float part = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -415,7 +404,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
       }
       const float ps = act ? fast_exp2(sv - m) : 0.f;
       lsum += half == 0 ? ps : 0.f;
-      const uint16_t* vself = Qs + (rows_per_item + kr) * HD;
+      const uint16_t* vself = Own + (rows_per_item + kr) * HD;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -428,9 +417,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
         }
     }
   }
-  __syncthreads();  // every wave is done with the own K and V in the query block
+  __syncthreads();  // every wave is done with the own K and V in the own-key block
   if (wave_active) {
-    // normalised output of this column into the query block, column layout
+    // normalised output of this column into the own-key block, column layout
     // with its chunk swizzle
     if (qvalid) {
       const float ltot = lsum + __shfl_xor(lsum, 32, 64);
@@ -442,7 +431,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
           uint2 o;
           o.x = pack_bf16x2(oacc[db][i4 * 4 + 0] * inv, oacc[db][i4 * 4 + 1] * inv);
           o.y = pack_bf16x2(oacc[db][i4 * 4 + 2] * inv, oacc[db][i4 * 4 + 3] * inv);
-          *reinterpret_cast<uint2*>(&Qs[qc * HD + (((db * 4 + i4) ^ cswz(qc)) << 3) + half * 4]) = o;
+          *reinterpret_cast<uint2*>(&Own[qc * HD + (((db * 4 + i4) ^ cswz(qc)) << 3) + half * 4]) = o;
         }
     }
   }
@@ -455,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
     const int col = c / CPR, slot = c % CPR;
     const int lr = col / G;
     if (lr < item_nrows) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&Qs[c * 8]);
+      const uint4 v = *reinterpret_cast<const uint4*>(&Own[c * 8]);
       *reinterpret_cast<uint4*>(obase + (size_t)lr * ldo + (col % G) * HD + ((slot ^ cswz(col)) << 3)) = v;
     }
   }

@@ -185,29 +185,38 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   // row = (r/4)*8 + half*4 + r%4, col = lane%32
   auto epilogue = [&](int m0, int n0) {
     if constexpr (EPI == EPI_RESID) {
-      // residual add, 8 of a lane's rows at a time: every load of the group is
-      // in flight before the first add (rows past M read row M - 1 and are not
-      // stored), so a group pays one memory latency instead of one per row
+      // residual add, software-pipelined over groups of GR of a lane's rows:
+      // the loads of group j + 1 are in flight while group j is added and
+      // stored, so the epilogue pays about one memory latency in all rather
+      // than one per group (rows past M read row M - 1 and are not stored)
       float* C = reinterpret_cast<float*>(Cv);
+      constexpr int GR = NI >= 4 ? 4 : 8;  // rows per group: GR x NI loads in flight per buffer
+      constexpr int NGR = MI * (16 / GR);
+      float xv[2][GR][NI];
+      auto row_of = [&](int j, int r) {
+        return m0 + wm * WTM + (j / (16 / GR)) * 32 + (((j % (16 / GR)) * GR + r) >> 2) * 8 + half * 4 + (r & 3);
+      };
+      auto load_group = [&](int j, int buf) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
+        for (int r = 0; r < GR; ++r) {
+          const int row = min(row_of(j, r), M - 1);
 #pragma unroll
-        for (int r0 = 0; r0 < 16; r0 += 8) {
-          float xv[8][NI];
+          for (int ni = 0; ni < NI; ++ni)
+            xv[buf][r][ni] = C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)];
+        }
+      };
+      load_group(0, 0);
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const int row = min(m0 + wm * WTM + mi * 32 + ((r0 + r) >> 2) * 8 + half * 4 + (r & 3), M - 1);
+      for (int j = 0; j < NGR; ++j) {
+        if (j + 1 < NGR) load_group(j + 1, (j + 1) & 1);
+        const int mi = j / (16 / GR), r0 = (j % (16 / GR)) * GR;
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) xv[r][ni] = C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)];
-          }
+        for (int r = 0; r < GR; ++r) {
+          const int row = row_of(j, r);
+          if (row < M) {
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const int row = m0 + wm * WTM + mi * 32 + ((r0 + r) >> 2) * 8 + half * 4 + (r & 3);
-            if (row < M) {
-#pragma unroll
-              for (int ni = 0; ni < NI; ++ni)
-                C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)] = xv[r][ni] + acc[mi][ni][r0 + r];
-            }
+            for (int ni = 0; ni < NI; ++ni)
+              C[(size_t)row * ldc + n0 + wn * WTN + ni * 32 + (lane & 31)] = xv[j & 1][r][ni] + acc[mi][ni][r0 + r];
           }
         }
       }

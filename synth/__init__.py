@@ -140,17 +140,32 @@ def make_weights(cfg: ModelConfig, seed: int = 0, gain_sigma: float = 0.0) -> Di
 
 
 def make_vid_table(cfg: ModelConfig, seed: int = 1, n_rows: int | None = None) -> np.ndarray:
-    """Synthetic frozen item vectors z_i, stored fp16 (uint16 bits), shape [N, d].
+    """Item table of the tiny ranker: rows ~ N(0, 0.02^2) i.i.d., stored fp16
+    (uint16 bits), shape [N, d].
 
-    Rows ~ N(0, 0.02^2) i.i.d., the scale of the token embedding, standing in
-    for the pages' interface output, whose rows are calibrated to the ranker's
-    native embedding scale.  (The export that makes such rows from encoder
-    outputs is a step of its own; its inputs come from encoder_outputs.)
+    The 0.6B-shaped ranker's table is made the way the pages make theirs
+    instead: encoder outputs (table_encoder_outputs) exported by the
+    continuous-input interface, RMS-normalised rows at the reference scale of
+    the token embedding (TABLE_GAMMA, TABLE_EPS below).  That export is model
+    arithmetic, so it is not done here: the library's export entry point makes
+    the GPU table and the oracle's export makes the oracle's.
     """
     n = cfg.n_vid if n_rows is None else n_rows
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
     g = rng.standard_normal((n, cfg.d_model), dtype=np.float32)
     return f32_to_f16_bits(g * np.float32(INIT_STD))
+
+
+# Export arguments of the 0.6B-shaped ranker's item table: gain e^gamma = 1
+# and the ranker's own RMSNorm epsilon; rho is the RMS of the token embedding.
+TABLE_GAMMA = 0.0
+TABLE_EPS = 1e-6
+
+
+def table_encoder_outputs(cfg: ModelConfig, seed: int = 1) -> np.ndarray:
+    """Encoder outputs a_i, float32 [N, d], whose export is the item table of
+    the 0.6B-shaped ranker (one row per VID)."""
+    return encoder_outputs(cfg.n_vid, cfg.d_model, seed=seed)
 
 
 def encoder_outputs(n_rows: int, d: int, seed: int = 11) -> np.ndarray:

@@ -2,10 +2,15 @@
 
 Score tolerance: |s_gpu - s_oracle| <= 2e-2 * max(1, |s_oracle|) (bf16 path
 against the float64 oracle); GPU MIS against GPU independent scoring:
-<= 1e-3 * max(1, |s|).  Top-10 order: a pair of candidates ordered differently
-by the GPU and the oracle is a failure only when their oracle scores differ
-by more than twice the request's largest measured score error (a closer pair
-cannot be told apart at the measured precision); strict swaps are reported.
+<= 1e-3 * max(1, |s|).
+
+Top-10 order: the strict criterion -- the GPU's top 10 equals the oracle's
+top 10, in order -- is reported (requests with a swap), not asserted.
+Random-init scores have near-ties closer than the bf16 path's score error,
+and a swap is always within the scores' own errors: if the GPU orders i
+above j while the oracle orders j above i, then |e_i| + |e_j| exceeds their
+oracle gap.  So any criterion that forgives swaps "explained by the measured
+error" can never fail and is not used; the score tolerance is the assertion.
 """
 import numpy as np
 
@@ -18,19 +23,22 @@ def score_err(gpu, ref):
     return float(np.max(np.abs(gpu - ref) / np.maximum(1.0, np.abs(ref))))
 
 
-def top10_check(gpu, ref, k=10):
-    """Returns (ok, n_strict_swaps)."""
-    gpu, ref = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+def _discordant_pairs(gpu, ref, k):
+    """Pairs among the union of both top-k lists that the two orderings rank
+    differently (with ties broken by candidate index)."""
     k = min(k, gpu.shape[0])
-    dmax = float(np.max(np.abs(gpu - ref)))
-    cand = np.union1d(np.argsort(-gpu, kind="stable")[:k], np.argsort(-ref, kind="stable")[:k])
-    strict = 0
-    ok = True
-    for i in cand:
-        for j in cand:
-            if i < j and (gpu[i] - gpu[j]) * (ref[i] - ref[j]) < 0:
-                strict += 1
-                if abs(ref[i] - ref[j]) > 2 * dmax:
-                    ok = False
-    same = np.array_equal(np.argsort(-gpu, kind="stable")[:k], np.argsort(-ref, kind="stable")[:k])
-    return ok, (0 if same else max(strict, 1))
+    order_g = np.argsort(-gpu, kind="stable")
+    order_r = np.argsort(-ref, kind="stable")
+    cand = np.union1d(order_g[:k], order_r[:k])
+    rank_g = np.empty_like(order_g)
+    rank_g[order_g] = np.arange(order_g.shape[0])
+    rank_r = np.empty_like(order_r)
+    rank_r[order_r] = np.arange(order_r.shape[0])
+    return [(i, j) for i in cand for j in cand if i < j and (rank_g[i] - rank_g[j]) * (rank_r[i] - rank_r[j]) < 0]
+
+
+def top10_strict_swaps(gpu, ref, k=10):
+    """Discordant pairs within the two top-k lists: 0 exactly when the GPU's
+    top k equals the oracle's top k in order."""
+    gpu, ref = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+    return len(_discordant_pairs(gpu, ref, k))

@@ -210,3 +210,52 @@ def test_layer_stages(fixture, layers, request):
         assert _bf16_close(h, g / (1 + np.exp(-g)) * (b @ W["w_up"].T))
         xo = r.stage(reqs, l, "layer_out").astype(np.float64)
         assert _rel(xo, xm + h @ W["w_down"].T) < 1e-5
+
+
+def _rope_and_attention_checks(model, cfg, reqs, r, rows, L, K):
+    """q/k norm + rotary and attention of layer 0 on the given packed rows of one
+    request, each against the oracle's building block applied to the GPU's own
+    input for that stage."""
+    H, Hk, hd, eps = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps
+    nq, nk = H * hd, Hk * hd
+    W = model.layers[0]
+    pos = mis_positions(L, K)
+    qkv = widen_bf16(r.stage(reqs, 0, "qkv"))
+    qr = widen_bf16(r.stage(reqs, 0, "qk_rope"))
+    n = rows.shape[0]
+    q_ref = rope_rotate(rmsnorm(qkv[rows, :nq].reshape(n, H, hd), W["q_norm"], eps), pos[rows], cfg.rope_base)
+    k_ref = rope_rotate(rmsnorm(qkv[rows, nq:nq + nk].reshape(n, Hk, hd), W["k_norm"], eps), pos[rows],
+                        cfg.rope_base)
+    assert _bf16_close(qr[rows, :nq], q_ref.reshape(n, nq))
+    assert _bf16_close(qr[rows, nq:nq + nk], k_ref.reshape(n, nk))
+    np.testing.assert_array_equal(qr[:, nq + nk:], qkv[:, nq + nk:])  # v untouched
+    att = widen_bf16(r.stage(reqs, 0, "attn"))
+    T = L + K
+    allowed = tree_mask(L, K)[rows]
+    att_ref = attention(qr[rows, :nq].reshape(n, H, hd), qr[:, nq:nq + nk].reshape(T, Hk, hd),
+                        qr[:, nq + nk:].reshape(T, Hk, hd), allowed).reshape(n, nq)
+    assert _bf16_close(att[rows], att_ref, floor=1e-2)  # P is rounded to bf16 before P.V
+
+
+def test_layer0_stress_shape_against_oracle(gpu_qwen):
+    # L = 4096, K = 512 (the stress request): rotary up to position 4096, prefix
+    # attention over 32 query tiles x 64 key tiles, branch tiles holding 128 of
+    # the 512 candidates, checked on every 7th prefix row and every candidate
+    cfg, w, D, model, r = gpu_qwen
+    (p, c), = _batch(cfg, 5, 1)
+    L, K = len(p), len(c)
+    assert (L, K) == (4096, 512)
+    rows = np.concatenate([np.arange(0, L, 7), np.arange(L - 64, L), np.arange(L, L + K)])
+    _rope_and_attention_checks(model, cfg, [(p, c)], r, np.unique(rows), L, K)
+
+
+def test_layer0_longest_prefix_against_oracle(gpu_qwen):
+    # the longest accepted prefix (L = 32767): the last prefix rows and the
+    # candidates, which sit at the rotary table's last position
+    cfg, w, D, model, r = gpu_qwen
+    (p, c), = _batch(cfg, 5, 1)
+    L = r.dims.max_prefix
+    prefix = np.resize(p, L).astype(np.int32)
+    cands = c[[0, 255, 511]]
+    rows = np.concatenate([np.arange(0, 64), np.arange(L - 200, L + 3)])
+    _rope_and_attention_checks(model, cfg, [(prefix, cands)], r, rows, L, len(cands))

@@ -1,11 +1,14 @@
 """End-to-end parity of the GPU MIS forward with the float64 oracle, at the
 workload shapes: tiny (L=48, K=8), one 0.6B request (L=452, K=100), a packed
-64-request varlen batch (sampled requests checked against the oracle), the
-K=8 rating mix, and the L=4096 / K=512 stress shape (checked against GPU
-independent scoring on sampled candidates).  Also: GPU MIS versus GPU
+64-request varlen batch (all 6,400 candidates against stored oracle scores),
+the K=8 rating mix, and the L=4096 / K=512 stress shape (sampled candidates
+against stored oracle scores and against GPU independent scoring).  Also: GPU MIS versus GPU
 independent scoring, graph replay versus eager launch, determinism, batch
 and permutation invariance, the error paths, and candidates spanning m rows
 (items of m vectors) against the oracle's m-row branches."""
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -13,11 +16,12 @@ import torch
 import synth
 from oracle import oracle_mis
 import shared_prefix_scoring_amd as spa
-from parity import MIS_VS_IND_TOL, SCORE_TOL, score_err, top10_check
+from parity import MIS_VS_IND_TOL, SCORE_TOL, score_err, top10_strict_swaps
 
 pytestmark = pytest.mark.gpu
 
 IND = spa.DUOLM_MODE_INDEPENDENT
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def reqs_of(cfg, cid, n=None, **kw):
@@ -40,11 +44,9 @@ def check_against_oracle(model, reqs, gpu_scores, which=None):
         ref = oracle_mis(model, p, c)
         e = score_err(per[i], ref)
         errs.append(e)
-        ok, s = top10_check(per[i], ref)
-        swaps += s
+        swaps += top10_strict_swaps(per[i], ref) > 0
         assert e <= SCORE_TOL, (i, e)
-        assert ok, i
-    print(f"max rel score err {max(errs):.3e}, requests with strict top-10 swaps: {swaps}")
+    print(f"max rel score err {max(errs):.3e}, requests with a strict top-10 swap: {swaps} of {len(errs)}")
     return max(errs)
 
 
@@ -74,18 +76,33 @@ def test_qwen_single_request(gpu_qwen):
     check_against_oracle(model, reqs, r.score(reqs))
 
 
-def test_qwen_c64_batch_sampled(gpu_qwen):
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_qwen_c64_batch_full_sweep(gpu_qwen):
+    # every one of the 6,400 candidates of a 64-request headline batch against
+    # the oracle's scores (written by tests/golden/make_golden.py from the
+    # oracle alone), in the two-lane serving configuration
     cfg, _, _, model, r = gpu_qwen
     reqs = reqs_of(cfg, 3, n=64)
+    g = golden("oracle_c64_batch.json")
+    assert g["prefix_len"] == [len(p) for p, _ in reqs]
     s = r.score(reqs)
     assert s.shape[0] == 6400 and np.all(np.isfinite(s))
-    lens = [len(p) for p, _ in reqs]
-    which = [int(np.argmin(lens)), int(np.argmax(lens)), 17]
-    check_against_oracle(model, reqs, s, which=which)
+    ref = np.asarray(g["scores"], np.float64)
+    per = np.asarray(split(s, reqs), np.float64)
+    rel = np.abs(per - ref) / np.maximum(1.0, np.abs(ref))
+    strict = sum(top10_strict_swaps(per[i], ref[i]) > 0 for i in range(len(reqs)))
+    print(f"c64 sweep: max rel err {rel.max():.3e}, p99 {np.percentile(rel, 99):.3e}, "
+          f"median {np.median(rel):.3e}, std of error {np.std(per - ref):.3e}; "
+          f"requests with a strict top-10 swap: {strict} of {len(reqs)}")
+    assert rel.max() <= SCORE_TOL
     # sampled requests scored alone give bit-identical scores (batch invariance)
-    per = split(s, reqs)
-    for i in which:
-        np.testing.assert_array_equal(r.score([reqs[i]]), per[i])
+    lens = [len(p) for p, _ in reqs]
+    for i in [int(np.argmin(lens)), int(np.argmax(lens)), 17]:
+        np.testing.assert_array_equal(r.score([reqs[i]]), per[i].astype(np.float32))
 
 
 def test_qwen_rating_mix(gpu_qwen):
@@ -106,12 +123,19 @@ def test_mis_vs_independent_qwen(gpu_qwen):
 
 
 def test_stress_shape_sampled(gpu_qwen):
-    # L = 4096, K = 512: MIS against independent scoring of sampled candidates
+    # L = 4096, K = 512: all 512 candidates by MIS, sampled ones against the
+    # oracle's scores of the same candidates scored on their own (candidates
+    # never see each other, so these equal the full-K scores) and against GPU
+    # independent scoring
     cfg, _, _, model, r = gpu_qwen
     (p, c), = reqs_of(cfg, 5, n=1)
     assert len(p) == 4096 and len(c) == 512
     mis = r.score([(p, c)])
-    pick = [0, 131, 300, 511]
+    g = golden("oracle_stress_subset.json")
+    pick = g["candidates"]
+    e = score_err(mis[pick], g["scores"])
+    print(f"stress shape: GPU MIS vs oracle on {len(pick)} candidates: {e:.3e}")
+    assert e <= SCORE_TOL
     ind = r.score([(p, c[pick])], mode=IND)
     e = score_err(mis[pick], ind)
     print(f"stress shape: MIS vs independent on {len(pick)} candidates: {e:.3e}")

@@ -253,3 +253,24 @@ def test_layer_matches_torch_composition(fixture, request):
     for layer in range(cfg.n_layers):
         ours = layer_stages(model, layer, x, pos, allowed)["x_out"]
         np.testing.assert_allclose(ours, torch_layer(model, layer, x, pos, allowed), rtol=1e-10, atol=1e-13)
+
+
+# ------------------------------------------------- top-10 order criteria ---
+
+
+def test_top10_strict_swaps():
+    from parity import top10_strict_swaps
+    ref = np.linspace(10.0, 0.0, 30)
+    assert top10_strict_swaps(ref, ref) == 0
+    g = ref.copy()
+    g[[3, 4]] = g[[4, 3]]                        # adjacent swap inside the top 10
+    assert top10_strict_swaps(g, ref) == 1
+    g[[0, 7]] = g[[7, 0]]                        # first and eighth trade places as well
+    assert top10_strict_swaps(g, ref) > 2
+    g3 = ref.copy()
+    g3[[20, 21]] = g3[[21, 20]]                  # a swap below the top 10 does not count
+    assert top10_strict_swaps(g3, ref) == 0
+    g4 = ref.copy()
+    g4[[9, 10]] = g4[[10, 9]]                    # 10th and 11th trade places
+    assert top10_strict_swaps(g4, ref) == 1
+    assert top10_strict_swaps(ref + 0.001 * np.arange(30) / 30, ref) == 0  # shifts that keep the order
