@@ -1,22 +1,31 @@
 """Throughput benchmark of the MIS ranker forward on one MI355X.
 
 Workload: the Qwen3-0.6B-shaped ranker (random init, bf16 weights, 200k-row
-fp16 item table) scoring batches of C = 64 synthetic requests packed varlen,
-K = 100 candidate VIDs each, history of 1/3/5/10 items with clip(Poisson(40),
-5, 120) feedback tokens per item.  One step = one duolm_score_batch_dev call
-over 64 requests (embedding gather, 28 decoder layers, score head), with the
-packed ids already resident in device memory.  Requests are consumed in order
-from a seeded pool of 10,000.  Closed loop: the next call starts when the
-previous one returns, so every request's latency is its call's duration.
+fp16 item table exported from synthetic encoder outputs by the library's own
+export entry point) scoring batches of C = 64 synthetic requests packed
+varlen, K = 100 candidate VIDs each, history of 1/3/5/10 items with
+clip(Poisson(40), 5, 120) feedback tokens per item.  One step = one
+duolm_score_batch_dev call over 64 requests (embedding gather, 28 decoder
+layers, score head), with the packed ids already resident in device memory.
+Requests are consumed in order from a seeded pool of 10,000.  Closed loop: the
+next call starts when the previous one returns.
 
-Prints one JSON line with scores/s, p99 latency, the roofline of the dominant
-kernel (timed with HIP events over the timed region) and the CPU oracle's rate
-on a bounded sample.
+Prints one JSON line: scores/s and p99 latency; the roofline of the dominant
+kernel and of every projection GEMM and of candidate-branch attention (timed
+live with HIP events on the launching stream); the pages' comparison points
+measured here (one-request latency, MIS against independent scoring at C = 1
+and C = 64, graph replay against eager launch at C = 1, 8 and 64); an open-loop
+Poisson run; and the CPU oracle's rate on bounded samples.
+
+Before each timed phase a 16-byte copy kernel (k_copy) is launched as a
+marker, so that a rocprofv3 kernel trace of this run can be cut into phases
+(python -m shared_prefix_scoring_amd.rocprof_summary trace DIR).
 """
 import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -28,7 +37,13 @@ import numpy as np  # noqa: E402
 METRIC = "candidate scores/sec on 1 MI355X (0.6B ranker, K=100, C=64); p99 ms"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-H100_PAGES = 26404.0        # pages' MIS + CUDA Graph figure, C=64, 100 candidates per request (H100)
+# The pages' figures on one H100 (trained model, Amazon Books, 100 candidates
+# per request; "DuoLM: Fast and Effective Personalized Recommendation with
+# Language Models", 实验结果 and the execution-mode ablation row of its results
+# table): context only, other hardware and data.
+PAGES = {"scores_per_s_c64": 26404.0, "scores_per_s_c1": 8870.0, "p99_ms_c1": 12.35, "p99_ms_c64": 536.9,
+         "independent_scores_per_s_c64": 851.48, "mis_gain_c1": 4.81, "mis_gain_c64": 29.3,
+         "graph_gain_c1": 3.54, "graph_gain_c64": 1.06}
 
 
 def log(msg):
@@ -43,26 +58,113 @@ def src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(cfg, w, D, reqs, budget_s):
-    """The float64 oracle, untuned, on consecutive requests of the same pool
-    until about budget_s of CPU time has been spent."""
-    from threadpoolctl import threadpool_info
+GEMM_SRC = ("k_gemm.hip", "common.h", "launch.h")
+ATTN_SRC = ("k_attn.hip", "common.h", "launch.h")
 
-    from oracle import OracleModel, oracle_mis
+
+def load_ranker(cfg, w):
+    """The ranker with its item table made by the library's export entry point
+    from the seeded encoder outputs (rho from the library's reference scale)."""
+    import torch
+    import shared_prefix_scoring_amd as spa
+    import synth
+    ranker = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
+    da = torch.from_numpy(synth.table_encoder_outputs(cfg)).cuda()
+    ranker.export_vid_table(da.data_ptr(), spa.DUOLM_DTYPE_F32, cfg.n_vid, ranker.reference_scale(),
+                            synth.TABLE_GAMMA, synth.TABLE_EPS)
+    del da
+    torch.cuda.empty_cache()
+    return ranker
+
+
+def host_table(ranker, cfg):
+    """The item table's rows on the host (for requests that ship their item
+    vectors inline), made by the library's export entry point."""
+    import torch
+    import shared_prefix_scoring_amd as spa
+    import synth
+    da = torch.from_numpy(synth.table_encoder_outputs(cfg)).cuda()
+    dz = torch.empty((cfg.n_vid, cfg.d_model), dtype=torch.int16, device="cuda")
+    spa.duolm_export_item_vectors(da.data_ptr(), spa.DUOLM_DTYPE_F32, cfg.n_vid, cfg.d_model,
+                                  ranker.reference_scale(), synth.TABLE_GAMMA, synth.TABLE_EPS, dz.data_ptr())
+    torch.cuda.synchronize()
+    return dz.cpu().numpy().view(np.uint16)
+
+
+def host_cpu():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    from threadpoolctl import threadpool_info
+    blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {"model": model, "os_cpu_count": os.cpu_count(), "blas_threads": blas}
+
+
+def cpu_baseline(cfg, w, pool, budget_s):
+    """The float64 oracle as written (untuned), on the host cores:
+      - value: consecutive requests of the headline pool until about budget_s
+        of wall time has been spent;
+      - the one-request workload (L = 452, K = 100), five repeats;
+      - brute-force independent scoring (one causal forward per candidate):
+        the tiny workload in full, and a stated subset of the one-request
+        workload's candidates (the full request is ~100x the subset).
+    The oracle's item table is its own export of the same encoder outputs;
+    building it and the oracle's weights is not timed."""
+    import synth
+    from oracle import OracleModel, brute_force_independent, export_table, oracle_mis, reference_scale, widen_bf16
+    a = synth.table_encoder_outputs(cfg)
+    rho = reference_scale(widen_bf16(w["embed"]))
+    D = np.empty(a.shape, np.uint16)
+    for i in range(0, a.shape[0], 16384):
+        D[i:i + 16384] = export_table(a[i:i + 16384], rho, synth.TABLE_GAMMA, synth.TABLE_EPS)
+    del a
     model = OracleModel.from_arrays(cfg, w, D)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    hc = host_cpu()
     n_scores, n_req = 0, 0
     t0 = time.perf_counter()
-    for r in reqs:
+    for r in pool:
         oracle_mis(model, r.prefix, r.cands)
         n_scores += r.K
         n_req += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": n_scores / dt, "unit": "candidate scores/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_req} requests ({n_scores} candidate scores) of the same pool, one at a time, "
-                      f"float64 NumPy, {dt:.1f} s"}
+    out = {"value": n_scores / dt, "unit": "candidate scores/s", "cores": hc["blas_threads"], "kind": "oracle",
+           "sample": f"{n_req} consecutive requests ({n_scores} candidate scores) of the headline pool, one at a "
+                     f"time, float64 NumPy, {dt:.1f} s", "host": hc}
+    (r2,) = synth.make_requests(2, cfg)
+    ts = []
+    for _ in range(5):
+        t1 = time.perf_counter()
+        oracle_mis(model, r2.prefix, r2.cands)
+        ts.append(time.perf_counter() - t1)
+    out["one_request_L452_K100"] = {"repeats": 5, "s_per_request_median": round(float(np.median(ts)), 3),
+                                    "scores_per_s": round(r2.K / float(np.median(ts)), 1)}
+    pick = [0, 1]
+    t1 = time.perf_counter()
+    brute_force_independent(model, r2.prefix, r2.cands, which=pick)
+    bf = (time.perf_counter() - t1) / len(pick)
+    out["brute_force_L452"] = {"sample": f"candidates {pick} of the one-request workload", "s_per_candidate": round(bf, 3),
+                               "scores_per_s": round(1.0 / bf, 3),
+                               "s_per_request_extrapolated": round(bf * r2.K, 1)}
+    tcfg = synth.TINY
+    tw = synth.make_weights(tcfg, seed=0)
+    tmodel = OracleModel.from_arrays(tcfg, tw, synth.make_vid_table(tcfg))
+    (rt,) = synth.make_requests(1, tcfg)
+    t1 = time.perf_counter()
+    brute_force_independent(tmodel, rt.prefix, rt.cands)
+    tb = time.perf_counter() - t1
+    t1 = time.perf_counter()
+    oracle_mis(tmodel, rt.prefix, rt.cands)
+    tm = time.perf_counter() - t1
+    out["tiny_L48_K8"] = {"brute_force_s": round(tb, 4), "oracle_mis_s": round(tm, 4)}
+    return out
 
 
 def open_loop(ranker, pack, rate, n_requests, seed, C, use_graph, stream):
@@ -430,276 +532,32 @@ def bench_session(ranker, cfg, steps):
     return out
 
 
-def summarize_counters(out_dir):
-    """Average of every counter of a rocprofv3 --pmc run (all counter_collection
-    csv files under out_dir) per kernel template, as markdown rows."""
-    import csv
-    acc = {}
-    for root, _, files in os.walk(out_dir):
-        for fn in files:
-            if not fn.endswith("counter_collection.csv"):
-                continue
-            with open(os.path.join(root, fn)) as f:
-                for r in csv.DictReader(f):
-                    n = r["Kernel_Name"]
-                    n = n.replace("duolm::", "").replace("(anonymous namespace)::", "").replace("void ", "")
-                    n = n[:n.index("(")] if "(" in n else n
-                    acc.setdefault(n, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    counters = sorted({c for v in acc.values() for c in v})
-    print("| kernel | dispatches | " + " | ".join(counters) + " |")
-    print("|---|---|" + "---|" * len(counters))
-    for n, v in sorted(acc.items()):
-        cells = [f"{sum(v[c]) / len(v[c]):.4g}" if c in v else "-" for c in counters]
-        print(f"| `{n}` | {len(next(iter(v.values())))} | " + " | ".join(cells) + " |")
+def gemm_roofline(stats, classes, name):
+    st = [stats[c] for c in classes if stats[c].launches]
+    launches = sum(x.launches for x in st)
+    if launches == 0:
+        return None
+    ms = sum(x.total_ms for x in st)
+    flops = sum(x.flops for x in st)
+    ach = flops / (ms * 1e-3) / 1e12
+    return {"kernel": name, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "launches": launches, "avg_launch_ms": round(ms / launches, 4),
+            "flops_per_launch": flops / launches, "ms_per_step": ms}
 
 
-def summarize_traffic(out_dir, warmup, steps, pool_size):
-    """Turn the four counter passes (FETCH_SIZE and WRITE_SIZE of the gate/up
-    GEMM in an eager `--no-graph --max-lanes 1 --open-loop 0 --cpu-baseline-s 0` run with the
-    given warmup/steps, and of the copy kernel under --calib-copy) into
-    profiles/traffic_gemm_gateup.json.  Each counter is scaled by what it
-    reads for the copy kernel's known bytes."""
-    import csv
-
-    import synth
-
-    def per_dispatch(d, counter, name_part):
-        vals = []
-        for root, _, files in os.walk(os.path.join(out_dir, d)):
-            for fn in files:
-                if not fn.endswith("counter_collection.csv"):
-                    continue
-                with open(os.path.join(root, fn)) as f:
-                    for r in csv.DictReader(f):
-                        if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
-                            vals.append(float(r["Counter_Value"]))
-        if not vals:
-            raise SystemExit(f"no {counter} rows for {name_part} under {d}")
-        return sum(vals) / len(vals), len(vals)
-
-    gate = "k_gemm<256, 256, 4, 2, 2>"
-    f_kib, n = per_dispatch("tr_f", "FETCH_SIZE", gate)
-    w_kib, _ = per_dispatch("tr_w", "WRITE_SIZE", gate)
-    cf_kib, _ = per_dispatch("cal_f", "FETCH_SIZE", "k_copy")
-    cw_kib, _ = per_dispatch("cal_w", "WRITE_SIZE", "k_copy")
-    copy_kib = (1 << 30) / 1024.0
-    fs, ws = copy_kib / cf_kib, copy_kib / cw_kib
-    cfg = synth.QWEN3_0P6B
-    pool = synth.make_requests(3, cfg, n_requests=pool_size)
-    calls = warmup + steps
-    # every eager call of the run, in order: warmup and timed steps, the pass
-    # without kernel timing, the branch-attention pass
-    seq = list(range(calls)) + list(range(warmup, calls)) + list(range(warmup, min(calls, warmup + 10)))
-    # each call: n_layers - 1 launches over all its rows, and the last layer's
-    # over the branch rows alone
-    rows = []
-    for i in seq:
-        reqs = pool[i * 64:(i + 1) * 64]
-        rows += [sum(r.L + r.K for r in reqs)] * (cfg.n_layers - 1) + [sum(r.K for r in reqs)]
-    if len(rows) != n:
-        raise SystemExit(f"{n} gate/up dispatches counted, {len(rows)} expected from the call sequence")
-    t_mean = sum(rows) / len(rows)
-    d, f = cfg.d_model, cfg.d_ffn
-    alg = 2 * f * d * 2 + t_mean * (d * 2 + f * 2)  # weights + activations in + SwiGLU out (bf16)
-    meas = (f_kib * fs + w_kib * ws) * 1024.0
-    out = {
-        "kernel": "k_gemm<256, 256, 4, 2, EPI_SWIGLU> (gate/up projection + SwiGLU epilogue)",
-        "workload": f"bench.py workload: 0.6B-shaped ranker, 64 requests x 100 candidates per call, eager launches, "
-                    f"{len(seq)} calls x {cfg.n_layers} layers",
-        "commands": [
-            "cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'k_gemm|k_copy' -d $REPO/gpurun_out/traffic/tr_f "
-            f"-o f -f csv -- python -u $REPO/bench.py --steps {steps} --warmup {warmup} --no-graph --max-lanes 1 --cpu-baseline-s 0 --open-loop 0",
-            "cd /tmp && rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'k_gemm|k_copy' -d $REPO/gpurun_out/traffic/tr_w "
-            f"-o w -f csv -- python -u $REPO/bench.py --steps {steps} --warmup {warmup} --no-graph --max-lanes 1 --cpu-baseline-s 0 --open-loop 0",
-            "cd /tmp && rocprofv3 --pmc FETCH_SIZE --kernel-include-regex k_copy -d $REPO/gpurun_out/traffic/cal_f -o f -f csv "
-            "-- python -u $REPO/bench.py --calib-copy",
-            "cd /tmp && rocprofv3 --pmc WRITE_SIZE --kernel-include-regex k_copy -d $REPO/gpurun_out/traffic/cal_w -o w -f csv "
-            "-- python -u $REPO/bench.py --calib-copy",
-            f"python bench.py --summarize-traffic gpurun_out/traffic --steps {steps} --warmup {warmup}",
-        ],
-        "calibration": {"copy_kernel": "k_copy, 1 GiB read + 1 GiB written",
-                        "FETCH_SIZE_KiB_per_launch": round(cf_kib, 1), "WRITE_SIZE_KiB_per_launch": round(cw_kib, 1),
-                        "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
-        "launches": n,
-        "mean_rows_per_launch": round(t_mean),
-        "FETCH_SIZE_KiB_per_launch": round(f_kib, 1),
-        "WRITE_SIZE_KiB_per_launch": round(w_kib, 1),
-        "bytes_per_launch": round(meas),
-        "algorithmic_bytes_per_launch": round(alg),
-        "ratio_measured_to_algorithmic": round(meas / alg, 2),
-        "kernel_src_hash": src_hash("k_gemm.hip", "common.h"),
-    }
-    path = os.path.join(ROOT, "profiles", "traffic_gemm_gateup.json")
-    with open(path, "w") as fh:
-        json.dump(out, fh, indent=1)
-        fh.write("\n")
-    print(json.dumps(out), flush=True)
-
-
-def summarize_trace(trace_dir, warmup, steps):
-    """Per-kernel summary of a rocprofv3 --kernel-trace run of the headline
-    bench (markdown rows on stdout): dispatches, average duration, the union of
-    the dispatch intervals (device time the kernel ran, counting concurrent
-    dispatches once), and the average over dispatches that ran alone (no other
-    dispatch overlapping them).  Then the gate/up GEMM's average over the
-    one-lane timed region alone, the launches the bench's HIP events time.
-    Every forward starts with one gather (k_embed); the bench runs warmup +
-    2 x steps two-lane calls (two forwards each), then `steps` one-lane calls
-    to prime the graphs, then the `steps` timed one-lane calls."""
-    import csv
-    rows = []
-    for root, _, files in os.walk(trace_dir):
-        for fn in files:
-            if fn.endswith("kernel_trace.csv"):
-                with open(os.path.join(root, fn)) as f:
-                    rows += list(csv.DictReader(f))
-    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
-    alone = []
-    hi = -1  # latest end among earlier dispatches
-    for i, (a, b, _) in enumerate(ev):
-        nxt = ev[i + 1][0] if i + 1 < len(ev) else b + 1
-        alone.append(a >= hi and b <= nxt)
-        hi = max(hi, b)
-
-    def short(n):
-        n = n.replace("duolm::", "").replace("(anonymous namespace)::", "").replace("void ", "")
-        return n[:n.index("(")] if "(" in n else n
-
-    stats = {}
-    for (a, b, n), solo in zip(ev, alone):
-        st = stats.setdefault(short(n), {"n": 0, "sum": 0, "iv": [], "solo": []})
-        st["n"] += 1
-        st["sum"] += b - a
-        st["iv"].append((a, b))
-        if solo:
-            st["solo"].append(b - a)
-    total = sum(st["sum"] for st in stats.values())
-    print("| kernel | dispatches | avg us | union ms | alone: dispatches, avg us | % of summed time |")
-    print("|---|---|---|---|---|---|")
-    for name, st in sorted(stats.items(), key=lambda kv: -kv[1]["sum"]):
-        u, lo, hi = 0, None, None
-        for a, b in sorted(st["iv"]):
-            if lo is None or a > hi:
-                if lo is not None:
-                    u += hi - lo
-                lo, hi = a, b
-            else:
-                hi = max(hi, b)
-        u += hi - lo
-        solo = st["solo"]
-        solo_txt = f"{len(solo)}, {sum(solo) / len(solo) / 1e3:.1f}" if solo else "0, -"
-        print(f"| `{name}` | {st['n']} | {st['sum'] / st['n'] / 1e3:.1f} | {u / 1e6:.2f} | {solo_txt} | "
-              f"{st['sum'] / total * 100:.1f} |")
-    fwd = sorted(int(r["Start_Timestamp"]) for r in rows if "k_embed" in r["Kernel_Name"])
-    gu = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
-                for r in rows if "k_gemm<256, 256, 4, 2, 2>" in r["Kernel_Name"])
-    first = 2 * (warmup + 2 * steps) + steps  # the first timed one-lane forward
-    if len(fwd) >= first + steps:
-        t0 = fwd[first]
-        t1 = fwd[first + steps] if len(fwd) > first + steps else float("inf")
-        win = [(a, b) for a, b in gu if t0 <= a < t1]
-        avg = sum(b - a for a, b in win) / max(len(win), 1) / 1e3
-        print()
-        print(f"one-lane timed region: {len(win)} gate/up dispatches ({steps} calls), avg {avg:.1f} us")
-
-
-def traffic_from_profile(kernel_hash):
-    p = os.path.join(ROOT, "profiles", "traffic_gemm_gateup.json")
+def traffic_from_profile(name, kernel_hash):
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_src_hash") != kernel_hash:
-        return None
-    return t.get("bytes_per_launch")
+    return t.get("bytes_per_launch") if t.get("kernel_src_hash") == kernel_hash else None
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--concurrency", type=int, default=64)
-    ap.add_argument("--pool", type=int, default=10_000, help="requests in the seeded pool")
-    ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--max-lanes", type=int, default=0,
-                    help="execution lanes of the timed region (0: library default, two halves for large calls; 1: one)")
-    ap.add_argument("--cpu-baseline-s", type=float, default=15.0, help="0 disables the oracle timing")
-    ap.add_argument("--open-loop", type=int, default=10_000,
-                    help="requests in the Poisson-arrival run (0 disables it)")
-    ap.add_argument("--breakdown", action="store_true", help="also time every kernel class (untimed pass)")
-    ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
-    ap.add_argument("--summarize-trace", metavar="DIR",
-                    help="print a per-kernel summary of a rocprofv3 --kernel-trace run under DIR (no GPU)")
-    ap.add_argument("--summarize-counters", metavar="DIR",
-                    help="print per-kernel averages of a rocprofv3 --pmc run under DIR (no GPU)")
-    ap.add_argument("--summarize-traffic", metavar="DIR",
-                    help="write profiles/traffic_gemm_gateup.json from the counter runs under DIR (no GPU)")
-    ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export", "packer", "session"],
-                    default="headline",
-                    help="headline: C=64 x K=100 (the metric); latency: one L=452 x K=100 request per call; "
-                         "rating: K=8 at C=8, graph vs eager and ids vs inline vectors; multivec: items of 8 "
-                         "vectors, K in {5,20,50,100}, C=1 and C=8; stress: L=4096 x K=512, MIS vs independent; "
-                         "export: the offline FP16 export of a 200k-row item table; packer: the host input "
-                         "packer and the host serving path; session: incremental history appends against "
-                         "prefix recompute")
-    args = ap.parse_args()
-
-    if args.summarize_counters:
-        summarize_counters(args.summarize_counters)
-        return
-    if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.warmup, args.steps)
-        return
-    if args.summarize_traffic:
-        summarize_traffic(args.summarize_traffic, args.warmup, args.steps, args.pool)
-        return
-
-    if args.gpus != 1:
-        print(json.dumps({"error": "the ranker runs on one GPU only; multi-GPU scaling is not implemented "
-                                   "(requests are independent, so the path would shard by request)",
-                          "n_gpus": args.gpus}), flush=True)
-        sys.exit(2)
-
+def headline(args, cfg, w, ranker):
     import torch
-
     import shared_prefix_scoring_amd as spa
     import synth
-
-    if args.calib_copy:
-        n = 1 << 30
-        a = torch.empty(n // 4, dtype=torch.int32, device="cuda").fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            spa.duolm_copy_device(b.data_ptr(), a.data_ptr(), n)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_each_way": n, "launches": 3}), flush=True)
-        return
-
-    cfg = synth.QWEN3_0P6B
-    log("generating weights and item table")
-    w = synth.make_weights(cfg, seed=0)
-    D = synth.make_vid_table(cfg)
-    ranker = spa.Ranker.from_blob(spa.weights_blob(cfg, w))
-    ranker.load_vid_table(D)
-    if args.workload != "headline":
-        if args.workload == "rating":
-            res = bench_rating(ranker, cfg, D, C=8, rounds=5)
-        elif args.workload == "latency":
-            res = bench_latency(ranker, cfg, calls=100)
-        elif args.workload == "multivec":
-            res = bench_multivec(ranker, cfg, rounds=3)
-        elif args.workload == "export":
-            res = bench_export(ranker, cfg, reps=20)
-        elif args.workload == "packer":
-            res = bench_packer(ranker, cfg)
-        elif args.workload == "session":
-            res = bench_session(ranker, cfg, steps=5)
-        else:
-            res = bench_stress(ranker, cfg, n_req=16, n_ind=32)
-        print(json.dumps({"workload": args.workload, **res}), flush=True)
-        ranker.close()
-        return
     log("generating requests")
     pool = synth.make_requests(3, cfg, n_requests=args.pool)
     C = args.concurrency
@@ -710,13 +568,18 @@ def main():
         ids, L, K = synth.pack_ids(reqs)
         batches.append((torch.from_numpy(ids).cuda(), L, K,
                         torch.empty(int(K.sum()), dtype=torch.float32, device="cuda")))
+    mark_src = torch.zeros(4, dtype=torch.int32, device="cuda")
+    mark_dst = torch.empty_like(mark_src)
     torch.cuda.synchronize()
     use_graph = not args.no_graph
     stream = torch.cuda.current_stream().cuda_stream
 
-    def call(b, lanes=0):
-        ranker.score_dev(b[1], b[2], b[0].data_ptr(), b[3].data_ptr(), use_graph=use_graph, stream=stream,
-                         max_lanes=lanes)
+    def marker():  # a 16-byte copy kernel: phase boundary in a kernel trace
+        spa.duolm_copy_device(mark_dst.data_ptr(), mark_src.data_ptr(), 16, stream)
+
+    def call(b, lanes=0, graph=use_graph, mode=0):
+        ranker.score_dev(b[1], b[2], b[0].data_ptr(), b[3].data_ptr(), use_graph=graph, stream=stream,
+                         max_lanes=lanes, mode=mode)
 
     def timed_steps(lanes):
         lat = []
@@ -737,39 +600,63 @@ def main():
         # batches fall in has its graphs captured
         for i in range(args.warmup, n_calls):
             call(batches[i], args.max_lanes)
-    # the timed region: the serving configuration, no kernel timing (a batch
-    # this size runs as two concurrent halves, one per execution lane)
+    # phase 1, the timed region: the serving configuration, no kernel timing
+    # (a batch this size runs as two concurrent halves, one per execution lane)
+    marker()
     dt, lat = timed_steps(args.max_lanes)
     n_scores = sum(int(b[2].sum()) for b in batches[args.warmup:])
     rows = [int(b[1].sum() + b[2].sum()) for b in batches[args.warmup:]]
     value = n_scores / dt
-    # the dominant kernel (gate/up GEMM), timed live with HIP events over a
-    # second timed region of the same steps run as one launch per call, so the
-    # kernel has the chip to itself (with two concurrent halves a launch's
-    # duration would include time the other half's kernels share the chip)
-    log("one-lane timed region (gate/up GEMM timing)")
-    ranker.set_profiling(["gemm_gateup"])
+    # phase 2: the projection GEMMs timed live with HIP event-record nodes
+    # around every launch, over a second timed region of the same steps run
+    # as one launch per call, so each kernel has the chip to itself (with two
+    # concurrent halves a launch's duration would include time the other
+    # half's kernels share the chip)
+    log("one-lane timed region (GEMM timing)")
+    gemm_classes = ["gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down"]
+    ranker.set_profiling(gemm_classes)
     if use_graph:
         for i in range(args.warmup, n_calls):
             call(batches[i], 1)
-        ranker.set_profiling(["gemm_gateup"])  # reset counters, keep the graphs
-    dt1, lat1 = timed_steps(1)
-    gu = ranker.kernel_stats("gemm_gateup")
-    # branch attention, one lane, its tiles launched on their own
+        ranker.set_profiling(gemm_classes)  # reset the counters, keep the graphs
+    marker()
+    dt1, _ = timed_steps(1)
+    stats = {c: ranker.kernel_stats(c) for c in gemm_classes}
+    # phase 3: candidate-branch attention, one lane, its tiles launched on
+    # their own (prefix tiles in a launch of their own beside them)
     ranker.set_profiling(["attn_branch"])
+    for i in range(args.warmup, min(n_calls, args.warmup + 10)):
+        call(batches[i], 1)  # captures the split-attention graphs
+    ranker.set_profiling(["attn_branch"])
+    marker()
     for i in range(args.warmup, min(n_calls, args.warmup + 10)):
         call(batches[i], 1)
     torch.cuda.synchronize()
     br = ranker.kernel_stats("attn_branch")
     ranker.set_profiling([])
-    if gu.launches == 0 or br.launches == 0:
+    if br.launches == 0 or any(st.launches == 0 for st in stats.values()):
         raise RuntimeError("no timed launches recorded for the roofline kernels")
-    gu_ms = gu.total_ms / max(gu.launches, 1)
-    gu_flops = gu.flops / max(gu.launches, 1)
-    br_ms = br.total_ms / max(br.launches, 1)
-    br_bytes = br.bytes / max(br.launches, 1)
-    achieved = gu_flops / (gu_ms * 1e-3) / 1e12
-    traffic = traffic_from_profile(src_hash("k_gemm.hip", "common.h"))
+    per = {"qkv": gemm_roofline(stats, ["gemm_qkv"], "k_gemm, QKV projection (bf16 store)"),
+           "o": gemm_roofline(stats, ["gemm_o"], "k_gemm, O projection (+ fp32 residual)"),
+           "gateup": gemm_roofline(stats, ["gemm_gateup"], "k_gemm, gate/up projection (+ SwiGLU)"),
+           "down": gemm_roofline(stats, ["gemm_down"], "k_gemm, down projection (+ fp32 residual)")}
+    # kernels (one template instantiation each at this shape): the residual
+    # epilogue GEMM serves both the O and the down projections
+    kernels = {"gemm_resid": gemm_roofline(stats, ["gemm_o", "gemm_down"],
+                                           "k_gemm residual-epilogue instantiation (O and down projections)"),
+               "gemm_gateup": per["gateup"], "gemm_qkv": per["qkv"]}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    roof = dict(kernels[dom])
+    roof["traffic"] = traffic_from_profile(dom, src_hash(*GEMM_SRC))
+    roof["timed"] = ("a second timed region over the same steps, one launch per call (no concurrent halves), HIP "
+                     "event-record nodes around every projection GEMM launch; the dominant kernel is the one with "
+                     "the most device time per step")
+    roof["ms_per_step"] = round(roof["ms_per_step"] / args.steps, 3)
+    for v in per.values():
+        v["ms_per_step"] = round(v["ms_per_step"] / args.steps, 3)
+    br_ms = br.total_ms / br.launches
+    br_bytes = br.bytes / br.launches
+    br_ach = br_bytes / (br_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -778,34 +665,33 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dt / args.steps * 1e3, 3),
-        "ms_per_step_one_lane_gateup_timed": round(dt1 / args.steps * 1e3, 3),
+        "ms_per_step_one_lane_gemm_timed": round(dt1 / args.steps * 1e3, 3),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / H100_PAGES, 3),
+        "vs_baseline": round(value / PAGES["scores_per_s_c64"], 3),
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "qwen3-0.6b-shaped ranker, C=64 requests x K=100 candidates, varlen prefixes",
                    "requests_per_step": C, "candidates_per_request": 100,
                    "execution_lanes": "two concurrent halves per call" if args.max_lanes != 1 else "one launch per call",
                    "mean_rows_per_step": round(float(np.mean(rows)), 1), "graph": use_graph,
-                   "graphs_primed": use_graph,
-                   "inputs": "packed ids resident in HBM"},
+                   "graphs_primed": use_graph, "inputs": "packed ids resident in HBM",
+                   "item_table": "200k x 1024 fp16, exported from seeded encoder outputs by the library"},
         "p99_ms": round(float(np.percentile(np.array(lat) * 1e3, 99)), 3),
         "closed_loop_call_ms": {"p50": round(float(np.percentile(np.array(lat) * 1e3, 50)), 3),
                                 "p99": round(float(np.percentile(np.array(lat) * 1e3, 99)), 3)},
-        "roofline": {"kernel": "gemm_gateup (k_gemm, SwiGLU epilogue)", "bound": "mfma",
-                     "timed": "a second timed region over the same steps, one launch per call (no concurrent "
-                              "halves), HIP event-record nodes around every gate/up launch",
-                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "avg_launch_ms": round(gu_ms, 4), "flops_per_launch": gu_flops},
-        "roofline_branch_attn": {"kernel": "attn_branch (k_attn, branch tiles)", "bound": "hbm",
-                                 "timed": "10 steps after the timed regions, one launch per call, branch tiles "
-                                          "launched on their own",
-                                 "achieved": round(br_bytes / (br_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                                 "unit": "GB/s", "frac": round(br_bytes / (br_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                                 "avg_launch_ms": round(br_ms, 4), "bytes_per_launch": br_bytes},
+        "roofline": roof,
+        "gemm_rooflines": per,
+        "roofline_branch_attn": {"kernel": "k_attn branch-only instantiation (candidate-branch tiles)", "bound": "hbm",
+                                 "timed": "10 one-launch calls after the timed regions, branch tiles launched on "
+                                          "their own, HIP event-record nodes around each launch",
+                                 "achieved": round(br_ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(br_ach / PEAK_HBM_GBS, 4), "launches": br.launches,
+                                 "avg_launch_ms": round(br_ms, 4), "bytes_per_launch": br_bytes,
+                                 "traffic": traffic_from_profile("attn_branch", src_hash(*ATTN_SRC))},
     }
+    if args.extras:
+        out["pages_comparisons"] = comparisons(args, cfg, ranker, batches, lat, marker, stream)
     if args.open_loop > 0:
         log("open-loop Poisson run")
         req_rate = value / 100.0 * 0.9
@@ -829,23 +715,159 @@ def main():
                             "path": "structured requests -> host packer -> page-locked staging -> "
                                     "scores to host (PCIe-inclusive)",
                             "warmup": "an untimed open loop of half as many requests, other arrivals"}
-    if args.breakdown:
-        ranker.set_profiling(spa.KERNEL_CLASSES)
-        for i in range(min(5, len(batches))):
-            ranker.score_dev(batches[i][1], batches[i][2], batches[i][0].data_ptr(), batches[i][3].data_ptr(),
-                             use_graph=False, stream=stream)
-        bd = {}
-        for k in spa.KERNEL_CLASSES:
-            st = ranker.kernel_stats(k)
-            if st.launches:
-                bd[k] = {"ms_per_step": round(st.total_ms / min(5, len(batches)), 3),
-                         "tflops": round(st.flops / (st.total_ms * 1e-3) / 1e12, 1) if st.flops else None,
-                         "gbs": round(st.bytes / (st.total_ms * 1e-3) / 1e9, 1)}
-        out["breakdown_eager"] = bd
-        ranker.set_profiling([])
     if args.cpu_baseline_s > 0:
         log("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(cfg, w, D, pool, args.cpu_baseline_s)
+        out["cpu_baseline"] = cpu_baseline(cfg, w, pool, args.cpu_baseline_s)
+    return out
+
+
+def comparisons(args, cfg, ranker, batches, lat_c64, marker, stream):
+    """The pages' comparison points measured on this path: one-request
+    latency, MIS against independent scoring (prefix recomputed per
+    candidate) at C = 1 and C = 64, graph replay against eager launch at C = 1,
+    8 and 64.  The pages' H100 figures ride along as context."""
+    import torch
+    import synth
+
+    def med_ms(fn, n, warm=2):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            t.append((time.perf_counter() - t0) * 1e3)
+        return np.array(t)
+
+    def dev(reqs):
+        ids, L, K = synth.pack_ids(reqs)
+        return (torch.from_numpy(ids).cuda(), L, K, torch.empty(int(K.sum()), dtype=torch.float32, device="cuda"))
+
+    def run(b, graph=True, mode=0):
+        ranker.score_dev(b[1], b[2], b[0].data_ptr(), b[3].data_ptr(), use_graph=graph, stream=stream, mode=mode)
+
+    out = {}
+    log("comparison points: one request (L = 452, K = 100)")
+    marker()
+    one = dev(synth.make_requests(2, cfg))
+    t_g = med_ms(lambda: run(one), 100, warm=5)
+    mis1 = one[3].clone()
+    t_e = med_ms(lambda: run(one, graph=False), 30)
+    t_i = med_ms(lambda: run(one, mode=1), 5)  # leaves the independent scores in one[3]
+    out["c1_latency"] = {"p50_ms": round(float(np.median(t_g)), 3), "p99_ms": round(float(np.percentile(t_g, 99)), 3),
+                         "scores_per_s": round(100 / float(np.median(t_g)) * 1e3, 1),
+                         "pages_h100": {"p99_ms": PAGES["p99_ms_c1"], "scores_per_s": PAGES["scores_per_s_c1"]}}
+    out["c1_graph_vs_eager"] = {"graph_ms": round(float(np.median(t_g)), 3), "eager_ms": round(float(np.median(t_e)), 3),
+                                "gain": round(float(np.median(t_e) / np.median(t_g)), 3),
+                                "pages_h100_gain": PAGES["graph_gain_c1"]}
+    out["c1_mis_vs_independent"] = {"mis_ms": round(float(np.median(t_g)), 3),
+                                    "independent_ms": round(float(np.median(t_i)), 3),
+                                    "gain": round(float(np.median(t_i) / np.median(t_g)), 2),
+                                    "max_abs_diff": float((one[3] - mis1).abs().max()),
+                                    "pages_h100_gain": PAGES["mis_gain_c1"]}
+    log("comparison points: C = 64 (independent scoring and eager launch of one headline batch)")
+    marker()
+    b0 = batches[args.warmup]
+    t_mis = float(np.median(np.array(lat_c64) * 1e3))
+    t_ind = med_ms(lambda: run(b0, mode=1), 2, warm=1)
+    ind = b0[3].clone()
+    run(b0)
+    torch.cuda.synchronize()
+    t_eag = med_ms(lambda: run(b0, graph=False), 5)
+    n = int(b0[2].sum())
+    out["c64_mis_vs_independent"] = {
+        "mis_ms": round(t_mis, 3), "independent_ms": round(float(np.median(t_ind)), 3),
+        "independent_scores_per_s": round(n / float(np.median(t_ind)) * 1e3, 1),
+        "gain": round(float(np.median(t_ind)) / t_mis, 2),
+        "independent_rows": int(sum((int(l) + 1) * int(k) for l, k in zip(b0[1], b0[2]))),
+        "max_abs_diff": float((b0[3] - ind).abs().max()),
+        "pages_h100": {"gain": PAGES["mis_gain_c64"], "independent_scores_per_s": PAGES["independent_scores_per_s_c64"]}}
+    out["c64_graph_vs_eager"] = {"graph_ms": round(t_mis, 3), "eager_ms": round(float(np.median(t_eag)), 3),
+                                 "gain": round(float(np.median(t_eag)) / t_mis, 3),
+                                 "pages_h100_gain": PAGES["graph_gain_c64"]}
+    log("comparison points: rating regime (C = 8, K = 8)")
+    marker()
+    rq = synth.make_requests(4, cfg)
+    rb = [dev(rq[i:i + 8]) for i in range(0, len(rq), 8)]
+    tg = med_ms(lambda: [run(b) for b in rb], 3, warm=1) / len(rb)
+    te = med_ms(lambda: [run(b, graph=False) for b in rb], 3, warm=1) / len(rb)
+    out["c8_k8_graph_vs_eager"] = {"graph_ms_per_call": round(float(np.median(tg)), 3),
+                                   "eager_ms_per_call": round(float(np.median(te)), 3),
+                                   "gain": round(float(np.median(te) / np.median(tg)), 3)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--concurrency", type=int, default=64)
+    ap.add_argument("--pool", type=int, default=10_000, help="requests in the seeded pool")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--max-lanes", type=int, default=0,
+                    help="execution lanes of the timed region (0: library default, two halves for large calls; 1: one)")
+    ap.add_argument("--cpu-baseline-s", type=float, default=12.0, help="0 disables the oracle timing")
+    ap.add_argument("--open-loop", type=int, default=10_000,
+                    help="requests in the Poisson-arrival run (0 disables it)")
+    ap.add_argument("--extras", type=int, default=1, help="0 skips the pages' comparison points")
+    ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
+    ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export", "packer", "session"],
+                    default="headline",
+                    help="headline: C=64 x K=100 (the metric); latency: one L=452 x K=100 request per call; "
+                         "rating: K=8 at C=8, graph vs eager and ids vs inline vectors; multivec: items of 8 "
+                         "vectors, K in {5,20,50,100}, C=1 and C=8; stress: L=4096 x K=512, MIS vs independent; "
+                         "export: the offline FP16 export of a 200k-row item table; packer: the host input "
+                         "packer and the host serving path; session: incremental history appends against "
+                         "prefix recompute")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "the ranker runs on one GPU only; multi-GPU scaling is not implemented "
+                                   "(requests are independent, so the path would shard by request)",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import shared_prefix_scoring_amd as spa
+    import synth
+
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.empty(n // 4, dtype=torch.int32, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            spa.duolm_copy_device(b.data_ptr(), a.data_ptr(), n)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n, "launches": 3}), flush=True)
+        return
+
+    cfg = synth.QWEN3_0P6B
+    log("generating weights; exporting the item table")
+    w = synth.make_weights(cfg, seed=0)
+    ranker = load_ranker(cfg, w)
+    if args.workload != "headline":
+        if args.workload == "rating":
+            res = bench_rating(ranker, cfg, host_table(ranker, cfg), C=8, rounds=5)
+        elif args.workload == "latency":
+            res = bench_latency(ranker, cfg, calls=100)
+        elif args.workload == "multivec":
+            res = bench_multivec(ranker, cfg, rounds=3)
+        elif args.workload == "export":
+            res = bench_export(ranker, cfg, reps=20)
+        elif args.workload == "packer":
+            res = bench_packer(ranker, cfg)
+        elif args.workload == "session":
+            res = bench_session(ranker, cfg, steps=5)
+        else:
+            res = bench_stress(ranker, cfg, n_req=16, n_ind=32)
+        print(json.dumps({"workload": args.workload, **res}), flush=True)
+        ranker.close()
+        return
+    out = headline(args, cfg, w, ranker)
     print(json.dumps(out), flush=True)
     ranker.close()
 

@@ -78,11 +78,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // exceeds it by more than that.
 constexpr float kLazyTau = 8.0f;
 
-template <int HD, int NW, int BKV>
+// BRANCH_ONLY: a launch of branch tiles alone (pcap = 0), compiled as an
+// instantiation of its own so that profiles tell it apart from the launches
+// that carry prefix tiles; every row runs the same arithmetic in both.
+template <int HD, int NW, int BKV, bool BRANCH_ONLY>
 __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ QKV, int ld,
                                                  uint16_t* __restrict__ O, int ldo, DevBatch b, int H,
                                                  int Hkv, float scale_log2, int pcap) {
-  const bool BRANCH = (int)blockIdx.x >= pcap;
+  const bool BRANCH = BRANCH_ONLY || (int)blockIdx.x >= pcap;
   const int idx = BRANCH ? (int)blockIdx.x - pcap : (int)blockIdx.x;
   constexpr int NKS = HD / 16;         // k-steps of the QK^T product
   constexpr int NDB = HD / 32;         // 32-dim blocks of the output
@@ -457,8 +460,12 @@ template <int HD>
 void launch_hd(hipStream_t s, int cap_p, int cap_b, const uint16_t* QKV, int ld, uint16_t* O, int ldo,
                DevBatch b, int H, int Hkv, float scale_log2) {
   const dim3 grid(cap_p + cap_b, Hkv);
-  hipLaunchKernelGGL((k_attn<HD, NW, BKV>), grid, dim3(NW * 64), 0, s, QKV, ld, O, ldo, b, H, Hkv, scale_log2,
-                     cap_p);
+  if (cap_p == 0)
+    hipLaunchKernelGGL((k_attn<HD, NW, BKV, true>), grid, dim3(NW * 64), 0, s, QKV, ld, O, ldo, b, H, Hkv,
+                       scale_log2, 0);
+  else
+    hipLaunchKernelGGL((k_attn<HD, NW, BKV, false>), grid, dim3(NW * 64), 0, s, QKV, ld, O, ldo, b, H, Hkv,
+                       scale_log2, cap_p);
 }
 
 }  // namespace

@@ -262,9 +262,12 @@ def test_no_table_is_estate(tiny):
 def test_profiling_counters(gpu_qwen):
     cfg, _, _, _, r = gpu_qwen
     reqs = reqs_of(cfg, 3, n=16)
+    base = r.score(reqs)
     r.set_profiling(["gemm_gateup", "attn_branch"])
     for g in (False, True):
-        r.score(reqs, use_graph=g)
+        # timing the branch tiles launches them apart from the prefix tiles
+        # (the branch-only instantiation of the attention kernel): same bits
+        np.testing.assert_array_equal(r.score(reqs, use_graph=g), base)
     st = r.kernel_stats("gemm_gateup")
     # a call this size runs as two concurrent halves (one launch each per layer)
     assert st.launches % (2 * cfg.n_layers) == 0 and st.launches >= 2 * cfg.n_layers and st.total_ms > 0
