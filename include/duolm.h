@@ -160,6 +160,31 @@ int duolm_score_batch_dev(duolm_ranker* r, const int32_t* prefix_len, const int3
                           const duolm_opts* opts);
 
 /*
+ * duolm_score_batch_dev without any allocation, for callers that cannot
+ * allocate memory (code running under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and results as
+ * duolm_score_batch_dev, but the call's activations, descriptor block and
+ * scores live in a fixed scratch array of 112 MiB per GPU, built into the
+ * library (each GPU the library runs on holds it until the process ends), and
+ * the call makes no device or pinned allocation.  The forward runs as one
+ * eager launch on the call's stream (opts->use_graph and opts->max_lanes are
+ * ignored).
+ *   Limit: the call's rows (sum of L + K*m in MIS mode, of K*(L + m) in
+ *   independent mode) must fit the scratch: 24,580 bytes per row for the
+ *   0.6B shape, about 4,700 rows, and one launch; larger calls return EINVAL
+ *   and write nothing.
+ *   Every call on one GPU shares that GPU's scratch, which keeps the last
+ *   call's contents: calls that overlap on one GPU (from several threads, or
+ *   several rankers on different streams) race and must be serialised by the
+ *   caller.
+ * Errors: as duolm_score_batch_dev, plus EINVAL for a call over the limit and
+ * ESTATE if the scratch could not be located when the ranker was loaded.
+ */
+int duolm_score_batch_dev_noalloc(duolm_ranker* r, const int32_t* prefix_len, const int32_t* n_cand,
+                                  const int32_t* cand_len, int32_t n_req, const int32_t* d_ids, float* d_scores,
+                                  const duolm_opts* opts);
+
+/*
  * Offline export of item vectors -- the step that fills the item table
  * before serving ([digest] 一句话总结 and 核心方法: the continuous-input
  * interface RMS-normalises the encoder's item representation a, calibrates it

@@ -36,6 +36,7 @@ from ._lib import (  # noqa: F401
     duolm_reference_scale,
     duolm_score_batch,
     duolm_score_batch_dev,
+    duolm_score_batch_dev_noalloc,
     duolm_score_packed,
     duolm_session_create,
     duolm_session_free,

@@ -82,6 +82,8 @@ EXPORTS = {
                                     C.POINTER(duolm_opts)]),
     "duolm_score_batch_dev": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
                                         C.c_void_p, C.POINTER(duolm_opts)]),
+    "duolm_score_batch_dev_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                        C.c_void_p, C.POINTER(duolm_opts)]),
     "duolm_set_profiling": (C.c_int, [C.c_void_p, C.c_uint32]),
     "duolm_get_kernel_stats": (C.c_int, [C.c_void_p, C.c_int32, C.POINTER(duolm_kernel_stats)]),
     "duolm_last_error": (C.c_char_p, []),
@@ -227,6 +229,15 @@ def duolm_score_batch_dev(r, prefix_len, n_cand, d_ids: int, d_scores: int, mode
     o = _opts(mode, use_graph, stream, max_lanes)
     _check(lib().duolm_score_batch_dev(r, L.ctypes.data, K.ctypes.data, None if M is None else M.ctypes.data,
                                        L.shape[0], C.c_void_p(d_ids), C.c_void_p(d_scores), C.byref(o)))
+
+
+def duolm_score_batch_dev_noalloc(r, prefix_len, n_cand, d_ids: int, d_scores: int, mode: int = DUOLM_MODE_MIS,
+                                  stream=None, cand_len=None) -> None:
+    L, K = _i32(prefix_len), _i32(n_cand)
+    M = None if cand_len is None else _cand_lens(L.shape[0], cand_len)
+    o = _opts(mode, False, stream, 1)
+    _check(lib().duolm_score_batch_dev_noalloc(r, L.ctypes.data, K.ctypes.data, None if M is None else M.ctypes.data,
+                                               L.shape[0], C.c_void_p(d_ids), C.c_void_p(d_scores), C.byref(o)))
 
 
 def duolm_set_profiling(r, class_mask: int) -> None:
@@ -463,6 +474,10 @@ class Ranker:
                   use_graph: bool = True, stream=None, cand_len=None, max_lanes: int = 0) -> None:
         duolm_score_batch_dev(self.h, prefix_len, n_cand, d_ids, d_scores, mode, use_graph, stream, cand_len,
                               max_lanes)
+
+    def score_dev_noalloc(self, prefix_len, n_cand, d_ids: int, d_scores: int, mode: int = DUOLM_MODE_MIS,
+                          stream=None, cand_len=None) -> None:
+        duolm_score_batch_dev_noalloc(self.h, prefix_len, n_cand, d_ids, d_scores, mode, stream, cand_len)
 
     def stage(self, reqs, layer: int, stage: str, mode: int = DUOLM_MODE_MIS, cand_len=None) -> np.ndarray:
         d = self.dims

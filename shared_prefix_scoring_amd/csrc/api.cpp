@@ -27,6 +27,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <set>
 #include <string>
 #include <thread>
@@ -39,7 +40,24 @@
 
 using namespace duolm;
 
+// ---------------------------------------------------------------------------
+// Scratch of duolm_score_batch_dev_noalloc: one fixed array per GPU, holding
+// that entry point's activations, descriptor block and scores (each GPU the
+// library runs on keeps it until the process ends).  In host code the name
+// `scratch` is a host-side stand-in, not a device address: kernels and copies
+// use the per-device address looked up once, with that device current, when a
+// ranker is loaded on it (scratch_ptr below).
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(112) << 20;
+constexpr size_t kScratchMetaBytes = size_t(1) << 20;  // the descriptor part (and its pinned staging)
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 
 thread_local std::string g_err;
 
@@ -181,6 +199,9 @@ struct duolm_ranker {
   int64_t n_vid = 0;
   // execution lanes: lane 0 runs on the call's stream, lane 1 on its own
   Lane lanes[kLanes];
+  // the no-allocation entry point's lane: its buffers are carved from the
+  // device's scratch per call; its pinned descriptor staging is made at load
+  Lane na;
   hipEvent_t ids_ready = nullptr;  // the call's ids are on the device (lane 1 waits for it)
   hipEvent_t call_t0 = nullptr;    // timing origin of the call's timed launches
   // call inputs/outputs
@@ -400,6 +421,10 @@ int create_from_blob(const void* blob, uint64_t nbytes, int dev, duolm_ranker** 
     if (e == hipSuccess) e = hipMalloc((void**)&R->d_err, sizeof(int32_t));
     if (e == hipSuccess) e = hipEventCreateWithFlags(&R->ids_ready, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreate(&R->call_t0);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&R->na.meta_free[0], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&R->na.meta_free[1], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&R->na.h_meta[0], kScratchMetaBytes);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&R->na.h_meta[1], kScratchMetaBytes);
     for (int li = 0; li < kLanes && e == hipSuccess; ++li) {
       Lane& Ln = R->lanes[li];
       e = hipEventCreateWithFlags(&Ln.meta_free[0], hipEventDisableTiming);
@@ -408,6 +433,16 @@ int create_from_blob(const void* blob, uint64_t nbytes, int dev, duolm_ranker** 
       if (e == hipSuccess && li > 0) e = hipStreamCreateWithFlags(&Ln.stream, hipStreamNonBlocking);
     }
     if (e != hipSuccess) rc = fail(DUOLM_EHIP, "stream/event setup: %s", hipGetErrorString(e));
+  }
+  if (rc == DUOLM_OK && dev < kMaxDevices) {
+    // the scratch's address on this device, once per device (this device is current)
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) rc = fail(DUOLM_EHIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+      else g_scratch_ptr[dev] = p;
+    }
   }
   if (rc != DUOLM_OK) {
     duolm_free_ranker(R);
@@ -686,6 +721,8 @@ struct Enq {
   hipStream_t s;
   std::vector<Timed>* timed;  // eager: where to record timing events (null: no timing)
   GraphEntry* capture;        // graph capture in progress (null: eager)
+  const int32_t* ids = nullptr;  // the call's ids on the device (null: the handle's id buffer)
+  float* out = nullptr;          // where the head writes the scores (null: the handle's score buffer)
   int stop_layer = -1, stop_stage = -1;
   bool stopped = false;
   bool brows = false;  // the launches being enqueued cover the branch rows only
@@ -756,7 +793,9 @@ void enqueue_forward(Enq& q, const Caps& c) {
   DevBatch b = dev_batch(R, *ln);
   const int32_t* dT = &b.hdr->T;
   const int32_t* dB = &b.hdr->n_brows;
-  q.run(DUOLM_K_EMBED, [&] { launch_embed(s, c.T, R->d_ids, b, R->embed, R->vid, R->d_inline, D.vocab, R->n_vid, d, ln->X, ln->pos); });
+  const int32_t* ids = q.ids ? q.ids : R->d_ids;
+  float* scores = q.out ? q.out : R->d_out;
+  q.run(DUOLM_K_EMBED, [&] { launch_embed(s, c.T, ids, b, R->embed, R->vid, R->d_inline, D.vocab, R->n_vid, d, ln->X, ln->pos); });
   if (q.stop(0, DUOLM_STAGE_EMBED)) return;
   for (int l = 0; l < D.n_layers; ++l) {
     const LayerW& W = R->layers[l];
@@ -813,7 +852,7 @@ void enqueue_forward(Enq& q, const Caps& c) {
     if (q.stop(l, DUOLM_STAGE_LAYER_OUT)) return;
   }
   if (q.stop_layer >= 0) return;
-  q.run(DUOLM_K_HEAD, [&] { launch_head(s, c.scores, ln->X, b, R->final_norm, R->head, R->d_out, d, eps); });
+  q.run(DUOLM_K_HEAD, [&] { launch_head(s, c.scores, ln->X, b, R->final_norm, R->head, scores, d, eps); });
 }
 
 // Upload one launch's descriptor block (pinned double buffer).
@@ -1682,6 +1721,79 @@ int duolm_score_batch_dev(duolm_ranker* R, const int32_t* prefix_len, const int3
   return score_impl(R, in, d_ids, true, d_scores, true, opts);
 }
 
+int duolm_score_batch_dev_noalloc(duolm_ranker* R, const int32_t* prefix_len, const int32_t* n_cand,
+                                  const int32_t* cand_len, int32_t n_req, const int32_t* d_ids, float* d_scores,
+                                  const duolm_opts* opts) {
+  if (!R || !prefix_len || !n_cand || !d_ids || !d_scores) return fail(DUOLM_EINVAL, "NULL argument");
+  int rc = mode_ok(opts);
+  if (rc) return rc;
+  const int mode = opts ? opts->mode : DUOLM_MODE_MIS;
+  hipStream_t s = (opts && opts->hip_stream) ? (hipStream_t)opts->hip_stream : R->stream;
+  CallInput in{prefix_len, n_cand, cand_len, n_req};
+  int64_t total_ids = 0, total_scores = 0;
+  if ((rc = validate_lengths(R, in, total_ids, total_scores))) return rc;
+  char* scr = R->device < kMaxDevices ? (char*)g_scratch_ptr[R->device] : nullptr;
+  if (!scr) return fail(DUOLM_ESTATE, "no scratch on device %d", R->device);
+  std::vector<Plan> plans;
+  build_plans(R, in, mode, plans, false);
+  if (plans.size() != 1)
+    return fail(DUOLM_EINVAL, "the call needs %zu launches; the no-allocation entry point runs one", plans.size());
+  const Plan& P = plans[0];
+  // carve the call's buffers from the scratch: descriptor block, scores, then
+  // the activations of exactly P.T rows
+  Lane& Ln = R->na;
+  auto a = [](size_t x) { return align_up(x, 256); };
+  size_t off = a(sizeof(CallHeader));
+  Ln.off_sro = off; off = a(off + (2 * P.seqs.size() + 1) * 4);
+  Ln.off_seq = off; off = a(off + P.seqs.size() * sizeof(SeqDesc));
+  Ln.off_pi = off; off = a(off + P.pitems.size() * sizeof(WorkItem));
+  Ln.off_bi = off; off = a(off + P.bitems.size() * sizeof(WorkItem));
+  Ln.off_hr = off; off = a(off + P.head_rows.size() * 4);
+  Ln.off_pt = off;
+  Ln.meta_bytes = off;
+  if (off > kScratchMetaBytes)
+    return fail(DUOLM_EINVAL, "descriptor of %zu bytes over the no-allocation limit of %zu", off, kScratchMetaBytes);
+  const auto& D = R->dims;
+  const size_t T = (size_t)P.T;
+  const size_t bX = a(T * D.d_model * 4), bXn = a(T * D.d_model * 2), bQ = a(T * R->nqkv * 2),
+               bO = a(T * D.n_heads * D.head_dim * 2), bH = a(T * D.d_ffn * 2), bP = a(T * 4),
+               bS = a((size_t)total_scores * 4);
+  const size_t need = kScratchMetaBytes + bS + bX + bXn + bQ + bO + bH + bP;
+  if (need > kScratchBytes)
+    return fail(DUOLM_EINVAL, "%zu rows need %zu bytes of scratch; the no-allocation entry point holds %zu "
+                "(about %zu rows of this model)", T, need, kScratchBytes,
+                (kScratchBytes - kScratchMetaBytes) / (size_t)(D.d_model * 6 + R->nqkv * 2 + D.n_heads * D.head_dim * 2 +
+                                                              D.d_ffn * 2 + 8));
+  HIP_TRY(hipSetDevice(R->device));
+  char* p = scr;
+  Ln.d_meta = p; p += kScratchMetaBytes;
+  float* out = (float*)p; p += bS;
+  Ln.X = (float*)p; p += bX;
+  Ln.Xn = (uint16_t*)p; p += bXn;
+  Ln.QKV = (uint16_t*)p; p += bQ;
+  Ln.Ob = (uint16_t*)p; p += bO;
+  Ln.Hb = (uint16_t*)p; p += bH;
+  Ln.pos = (int32_t*)p;
+  Ln.cap_T = P.T;
+  if (s != R->stream) HIP_TRY(hipStreamSynchronize(R->stream));
+  R->call_n_inline = 0;
+  launch_fill_i32(s, R->d_err, 1, 0);
+  if ((rc = upload_plan(R, Ln, P, s))) return rc;
+  Caps c{P.T, (int)P.seqs.size(), (int)P.pitems.size(), (int)P.bitems.size(), (int)P.head_rows.size(),
+         0, 0, P.TB, 1};
+  Enq q{R, &Ln, s, nullptr, nullptr};
+  q.ids = d_ids;
+  q.out = out;
+  enqueue_forward(q, c);
+  HIP_TRY(hipGetLastError());
+  HIP_TRY(hipMemcpyAsync(R->h_err, R->d_err, 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (*R->h_err) return fail(DUOLM_ERANGE, "an id in the device batch is outside [0, V + N)");
+  HIP_TRY(hipMemcpyAsync(d_scores, out, (size_t)total_scores * 4, hipMemcpyDeviceToDevice, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return DUOLM_OK;
+}
+
 int duolm_set_profiling(duolm_ranker* R, uint32_t mask) {
   if (!R) return fail(DUOLM_EINVAL, "NULL argument");
   if (mask != R->prof_mask) drop_graphs(R);  // captured graphs carry their timing events
@@ -1719,6 +1831,10 @@ void duolm_free_ranker(duolm_ranker* R) {
       if (h) (void)hipHostFree(h);
     if (Ln.stream) (void)hipStreamDestroy(Ln.stream);
   }
+  for (hipEvent_t e : R->na.meta_free)
+    if (e) (void)hipEventDestroy(e);
+  for (char* h : R->na.h_meta)
+    if (h) (void)hipHostFree(h);  // the na lane's device buffers are the scratch: never freed
   if (R->wblob) (void)hipFree(R->wblob);
   if (R->vid) (void)hipFree(R->vid);
   if (R->d_ids) (void)hipFree(R->d_ids);

@@ -293,4 +293,17 @@ void launch_copy(hipStream_t s, void* dst, const void* src, size_t nbytes) {
   hipLaunchKernelGGL(k_copy, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)dst, (const uint4*)src, n);
 }
 
+// ---------------------------------------------------------------------------
+// Fill n int32 values (clears flags with a kernel rather than a memset node).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t* __restrict__ p, int n, int32_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+void launch_fill_i32(hipStream_t s, int32_t* p, int n, int32_t v) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+}
+
 }  // namespace duolm
