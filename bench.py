@@ -564,7 +564,8 @@ def headline(args, cfg, w, ranker):
     n_calls = args.warmup + args.steps
     batches = []
     for i in range(n_calls):
-        reqs = [pool[(i * C + j) % len(pool)] for j in range(C)]
+        k = 0 if args.same_batch else i
+        reqs = [pool[(k * C + j) % len(pool)] for j in range(C)]
         ids, L, K = synth.pack_ids(reqs)
         batches.append((torch.from_numpy(ids).cuda(), L, K,
                         torch.empty(int(K.sum()), dtype=torch.float32, device="cuda")))
@@ -654,6 +655,8 @@ def headline(args, cfg, w, ranker):
     roof["ms_per_step"] = round(roof["ms_per_step"] / args.steps, 3)
     for v in per.values():
         v["ms_per_step"] = round(v["ms_per_step"] / args.steps, 3)
+    per["qkv"]["traffic"] = traffic_from_profile("gemm_qkv", src_hash(*GEMM_SRC))
+    per["gateup"]["traffic"] = traffic_from_profile("gemm_gateup", src_hash(*GEMM_SRC))
     br_ms = br.total_ms / br.launches
     br_bytes = br.bytes / br.launches
     br_ach = br_bytes / (br_ms * 1e-3) / 1e9
@@ -813,6 +816,8 @@ def main():
     ap.add_argument("--open-loop", type=int, default=10_000,
                     help="requests in the Poisson-arrival run (0 disables it)")
     ap.add_argument("--extras", type=int, default=1, help="0 skips the pages' comparison points")
+    ap.add_argument("--same-batch", action="store_true",
+                    help="every call scores the pool's first 64 requests (counter runs: one geometry per kernel)")
     ap.add_argument("--calib-copy", action="store_true", help="run only the copy kernel (counter calibration)")
     ap.add_argument("--workload", choices=["headline", "latency", "rating", "multivec", "stress", "export", "packer", "session"],
                     default="headline",

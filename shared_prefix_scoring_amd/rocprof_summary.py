@@ -11,13 +11,24 @@
     python -m shared_prefix_scoring_amd.rocprof_summary counters DIR
         Per-kernel averages of every counter of a --pmc run.
 
-    python -m shared_prefix_scoring_amd.rocprof_summary traffic DIR --kernel NAME --work FILE
+    python -m shared_prefix_scoring_amd.rocprof_summary traffic DIR --kernel NAME --which W
         HBM traffic per dispatch of one kernel from four --pmc passes under
         DIR (fetch/ and write/: FETCH_SIZE and WRITE_SIZE of the workload;
         cal_fetch/ and cal_write/: the same counters of a 1 GiB copy), each
-        counter scaled by what it reads for the copy's known bytes.  FILE is
-        the JSON line the profiled benchmark pass printed (algorithmic bytes
-        per launch of the kernel's class); the result goes to stdout as JSON.
+        counter scaled by what it reads for the copy's known bytes, against
+        the algorithmic bytes per dispatch (see alg-bytes); JSON on stdout.
+
+    python -m shared_prefix_scoring_amd.rocprof_summary alg-bytes --which W
+        Algorithmic HBM bytes per dispatch when every call scores the
+        headline pool's first 64 requests (bench.py --same-batch), for
+        W = attn_branch (a branch-only attention launch: every request's
+        prefix K and V once per KV head, each candidate's query, own K/V and
+        output), gemm_resid (the residual-epilogue GEMM, the average of an O
+        and a down projection over all rows: weights, activations in, the
+        fp32 residual read and written), gemm_gateup or gemm_qkv (weights,
+        activations in, bf16 output).  The JSON also records a hash of the
+        kernel's sources, so that a benchmark on changed kernels reports no
+        traffic.
 """
 from __future__ import annotations
 
@@ -123,16 +134,51 @@ def _per_dispatch(d: str, counter: str, kernel: str):
     return sum(vals) / len(vals), len(vals)
 
 
-def traffic(d: str, kernel: str, work: str) -> None:
+def alg_bytes(which: str) -> float:
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import synth
+    cfg = synth.QWEN3_0P6B
+    reqs = synth.make_requests(3, cfg, n_requests=64)
+    H, Hk, hd, d, F = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.d_model, cfg.d_ffn
+    if which == "attn_branch":
+        return float(sum(r.L * Hk * hd * 4 + r.K * (H * hd * 2 + Hk * hd * 4 + H * hd * 2) for r in reqs))
+    T = sum(r.L + r.K for r in reqs)
+    if which == "gemm_resid":
+        o = (d * H * hd + T * H * hd) * 2 + T * d * 8
+        down = (d * F + T * F) * 2 + T * d * 8
+        return (o + down) / 2.0
+    if which == "gemm_gateup":
+        return float((2 * F * d + T * d + T * F) * 2)
+    if which == "gemm_qkv":
+        nq = (H + 2 * Hk) * hd
+        return float((nq * d + T * d + T * nq) * 2)
+    raise SystemExit(f"unknown kernel class {which}")
+
+
+SOURCES = {"attn_branch": ("k_attn.hip", "common.h", "launch.h"),
+           "gemm_resid": ("k_gemm.hip", "common.h", "launch.h"),
+           "gemm_gateup": ("k_gemm.hip", "common.h", "launch.h"),
+           "gemm_qkv": ("k_gemm.hip", "common.h", "launch.h")}
+
+
+def src_hash(which: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in SOURCES[which]:
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(d: str, kernel: str, which: str) -> None:
     f_kib, n = _per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", kernel)
     w_kib, _ = _per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", kernel)
     cf_kib, _ = _per_dispatch(os.path.join(d, "cal_fetch"), "FETCH_SIZE", "k_copy")
     cw_kib, _ = _per_dispatch(os.path.join(d, "cal_write"), "WRITE_SIZE", "k_copy")
     copy_kib = (1 << 30) / 1024.0
     fs, ws = copy_kib / cf_kib, copy_kib / cw_kib
-    with open(work) as f:
-        w = json.loads(f.read().strip().splitlines()[-1])
-    alg = w["bytes_per_launch"]
+    alg = alg_bytes(which)
     meas = (f_kib * fs + w_kib * ws) * 1024.0
     print(json.dumps({
         "kernel": kernel,
@@ -144,7 +190,7 @@ def traffic(d: str, kernel: str, work: str) -> None:
         "bytes_per_launch": round(meas),
         "algorithmic_bytes_per_launch": round(alg),
         "ratio_measured_to_algorithmic": round(meas / alg, 3),
-        "kernel_src_hash": w.get("kernel_src_hash"),
+        "kernel_src_hash": src_hash(which),
     }, indent=1))
 
 
@@ -156,14 +202,17 @@ def main() -> None:
     t = sub.add_parser("traffic")
     t.add_argument("dir")
     t.add_argument("--kernel", required=True, help="kernel name as in the trace table, e.g. 'k_gemm<192, 256, 2, 4, 1>'")
-    t.add_argument("--work", required=True, help="JSON line printed by the profiled benchmark pass")
+    t.add_argument("--which", required=True, choices=list(SOURCES))
+    sub.add_parser("alg-bytes").add_argument("--which", required=True, choices=list(SOURCES))
     a = ap.parse_args()
     if a.cmd == "trace":
         trace(a.dir)
     elif a.cmd == "counters":
         counters(a.dir)
+    elif a.cmd == "alg-bytes":
+        print(alg_bytes(a.which))
     else:
-        traffic(a.dir, a.kernel, a.work)
+        traffic(a.dir, a.kernel, a.which)
 
 
 if __name__ == "__main__":
