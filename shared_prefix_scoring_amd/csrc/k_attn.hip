@@ -258,6 +258,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   issue_own();
   wait_loads();
   __syncthreads();
+  // Every load has landed (above); telling the compiler that the query
+  // fragments are consumed here keeps its own wait for them (which would
+  // count the key-tile loads in flight) out of the tile loop.
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(qf[ks]));
 
   auto tile = [&](int t, auto st) {
     constexpr int ST = decltype(st)::value;
@@ -306,12 +311,15 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
     } else {
+      // key k0 + kb*32 + (r/4)*8 + half*4 + r%4 is visible when it is at or
+      // below klim (for every row kind klim < kend): one compare of the
+      // register's constant offset against the lane's bound
+      const int lim = klim - k0 - half * 4;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = k0 + kb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          const float v = (kk <= klim && kk < kend) ? s[kb][r] : -INFINITY;
+          const float v = (kb * 32 + (r >> 2) * 8 + (r & 3)) <= lim ? s[kb][r] : -INFINITY;
           s[kb][r] = v;
           tmax = fmaxf(tmax, v);
         }
@@ -385,12 +393,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
       const bool act = e < nmerge;
       const int kr = act ? lrow - nmerge + 1 + e : lrow;
       const uint16_t* kself = Own + kr * HD;
+      // q . k over the lane's half of the dims, two products per instruction
+      // (v_dot2c_f32_bf16: bf16 products are exact in fp32)
       float part = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(kself + (((ks * 2 + half) ^ cswz(kr)) << 3));
 #pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) part = __builtin_fmaf((float)qf[ks][e8], (float)kv[e8], part);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const bf16x2_t qa = {qf[ks][2 * e2], qf[ks][2 * e2 + 1]};
+          const bf16x2_t kb2 = {kv[2 * e2], kv[2 * e2 + 1]};
+          part = __builtin_amdgcn_fdot2_f32_bf16(qa, kb2, part, false);
+        }
       }
       const float dot = part + __shfl_xor(part, 32, 64);
       const float sv = dot * scale_log2;
