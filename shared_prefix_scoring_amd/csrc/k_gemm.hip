@@ -369,7 +369,10 @@ bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, 
   // the residual projections (N = 1024: 336 tiles of 256 rows at T = 21.5k, a
   // two-round launch whose second round is a third full) 192-row tiles finish
   // in the same number of rounds with 3/4 of the work each, and are used
-  // when they need fewer row-rounds.  (With the bf16 and SwiGLU epilogues the
+  // when they need fewer row-rounds -- for a launch that has the chip to
+  // itself: beside the other half of a two-lane call, whose kernels fill the
+  // last round's idle CUs, 256-row tiles measured faster (22.40 against
+  // 22.59 ms per 64-request call).  (With the bf16 and SwiGLU epilogues the
   // 192-row tile measured slower.)
   // CUs this launch can expect: with `share` launches side by side (the
   // halves of a batch on two streams) a tile size that fills its share fills
@@ -379,7 +382,7 @@ bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, 
   const long tiles256 = (long)((cap_m + 255) / 256) * nt;
   const long tiles128 = (long)((cap_m + 127) / 128) * (N % 128 == 0 ? N / 128 : 0);
   auto row_rounds = [&](int bm) { return ((((long)cap_m + bm - 1) / bm) * nt + ncu - 1) / ncu * bm; };
-  if (nt && tiles256 >= ncu && epi == EPI_RESID && row_rounds(192) < row_rounds(256))
+  if (nt && tiles256 >= ncu && epi == EPI_RESID && share <= 1 && row_rounds(192) < row_rounds(256))
     launch_cfg<192, 256, 2, 4>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else if (nt && tiles256 >= ncu)
     launch_cfg<256, 256, 4, 2>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
