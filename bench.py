@@ -17,9 +17,12 @@ measured here (one-request latency, MIS against independent scoring at C = 1
 and C = 64, graph replay against eager launch at C = 1, 8 and 64); an open-loop
 Poisson run; and the CPU oracle's rate on bounded samples.
 
-Before each timed phase a 16-byte copy kernel (k_copy) is launched as a
-marker, so that a rocprofv3 kernel trace of this run can be cut into phases
-(python -m shared_prefix_scoring_amd.rocprof_summary trace DIR).
+Before each phase a 16-byte copy kernel (k_copy) is launched as a marker, so
+that a rocprofv3 kernel trace of this run can be cut into phases (python -m
+shared_prefix_scoring_amd.rocprof_summary trace DIR): 1 the serving timed
+region, 2 capture of the one-lane graphs, 3 the one-lane timed region (the
+GEMM rooflines), 4 capture of the split-attention graphs, 5 the
+branch-attention timing, then the comparison points.
 """
 import argparse
 import hashlib
@@ -603,7 +606,7 @@ def headline(args, cfg, w, ranker):
             call(batches[i], args.max_lanes)
     # phase 1, the timed region: the serving configuration, no kernel timing
     # (a batch this size runs as two concurrent halves, one per execution lane)
-    marker()
+    marker()  # phase 1
     dt, lat = timed_steps(args.max_lanes)
     n_scores = sum(int(b[2].sum()) for b in batches[args.warmup:])
     rows = [int(b[1].sum() + b[2].sum()) for b in batches[args.warmup:]]
@@ -616,20 +619,22 @@ def headline(args, cfg, w, ranker):
     log("one-lane timed region (GEMM timing)")
     gemm_classes = ["gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down"]
     ranker.set_profiling(gemm_classes)
+    marker()  # phase 2: capture of the one-lane graphs
     if use_graph:
         for i in range(args.warmup, n_calls):
             call(batches[i], 1)
         ranker.set_profiling(gemm_classes)  # reset the counters, keep the graphs
-    marker()
+    marker()  # phase 3: the one-lane timed region
     dt1, _ = timed_steps(1)
     stats = {c: ranker.kernel_stats(c) for c in gemm_classes}
     # phase 3: candidate-branch attention, one lane, its tiles launched on
     # their own (prefix tiles in a launch of their own beside them)
     ranker.set_profiling(["attn_branch"])
+    marker()  # phase 4: capture of the split-attention graphs
     for i in range(args.warmup, min(n_calls, args.warmup + 10)):
-        call(batches[i], 1)  # captures the split-attention graphs
+        call(batches[i], 1)
     ranker.set_profiling(["attn_branch"])
-    marker()
+    marker()  # phase 5: the branch-attention timing
     for i in range(args.warmup, min(n_calls, args.warmup + 10)):
         call(batches[i], 1)
     torch.cuda.synchronize()
