@@ -68,7 +68,8 @@ template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restrict__ A, int lda,
                                                       const uint16_t* __restrict__ W, int ldw,
                                                       void* __restrict__ Cv, int ldc,
-                                                      const int32_t* __restrict__ dM, int N, int K) {
+                                                      const int32_t* __restrict__ dM, int N, int K,
+                                                      int xg) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MI = WTM / 32, NI = WTN / 32;
@@ -81,23 +82,55 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
 
   const int M = *dM;
   const int n_tiles = N / BN;
-  const int total = (M + BM - 1) / BM * n_tiles;
-  if ((int)blockIdx.x >= total) return;
+  const int nblk = __builtin_amdgcn_readfirstlane(gridDim.x);
+  // Tile order.  Workgroups are dispatched to the 8 XCDs round-robin
+  // (workgroup b on XCD b % 8), and each XCD has its own L2.  With xg > 0
+  // the column tiles are split into xg groups; XCD x works only on group
+  // x % xg, and takes the group's tiles (row-major) in runs of consecutive
+  // tiles, so the workgroups of one XCD share their A row blocks and their
+  // group's weight columns in that XCD's L2.  Round k hands out the group's
+  // tiles [k stride, (k + 1) stride): a full round gives each of the group's
+  // nx XCDs a run of `per` tiles (one per workgroup); a partial last round is
+  // split into nx runs as equal as can be, so no XCD is left holding the
+  // tail while another idles (a second launch beside this one waits for the
+  // XCD its next workgroup is dispatched to).
+  int grp = 0, q = 0, j = blockIdx.x, per = nblk, nx = 1, stride = nblk, ncol = n_tiles;
+  if (xg > 0 && nblk % 8 == 0 && n_tiles % xg == 0 && 8 % xg == 0) {
+    const int x = blockIdx.x % 8;
+    per = nblk / 8;
+    nx = 8 / xg;
+    grp = x % xg;
+    q = x / xg;
+    j = blockIdx.x / 8;
+    stride = nblk / xg;
+    ncol = n_tiles / xg;
+  }
+  const int total = (M + BM - 1) / BM * ncol;  // tiles of this workgroup's group
+  // index (row-major within the group) of this workgroup's tile in round k, or -1
+  auto tile_at = [&](int k) -> int {
+    const int base = k * stride;
+    if (base + stride <= total) return base + q * per + j;
+    const int r = total - base;
+    if (r <= 0) return -1;
+    const int chunk = (r + nx - 1) / nx;
+    return j < chunk && q * chunk + j < r ? base + q * chunk + j : -1;
+  };
+  const int first = tile_at(0);
+  if (first < 0) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5;
   const int KT = K / BK;
-  const int nblk = __builtin_amdgcn_readfirstlane(gridDim.x);
 
   // Load cursor: tile lt, slab lk go out next.  Per-lane source of this
   // wave's row groups: row g*8 + lane/8, the chunk whose swizzled slot is lane%8
   const uint16_t* pa[GA];
   const uint16_t* pb[GB];
-  int lt = blockIdx.x, lk = 0;
+  int lt = first, lround = 0, lk = 0;
   auto aim = [&](int tt) {
-    const int m0 = tt / n_tiles * BM, n0 = tt % n_tiles * BN;
+    const int m0 = tt / ncol * BM, n0 = (grp * ncol + tt % ncol) * BN;
 #pragma unroll
     for (int j = 0; j < GA; ++j) {
       const int r = (wave + NW * j) * 8 + (lane >> 3);
@@ -115,8 +148,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   auto advance = [&]() {
     if (++lk == KT) {
       lk = 0;
-      lt += nblk;
-      if (lt < total) aim(lt);
+      lt = tile_at(++lround);
+      if (lt >= 0) aim(lt);
     }
   };
   lds_u16_t* lds = (lds_u16_t*)(lds_void_t*)smem;
@@ -297,16 +330,16 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
 #pragma unroll
   for (int j = 0; j < NR; ++j) read_one(j, 0, 0, 0);
   int st = 0;
-  for (int ct = blockIdx.x;;) {
+  for (int ct = first, cround = 0;;) {
     for (int kt = 0; kt + 1 < KT; ++kt) {
       slab(st, std::false_type{});
       st ^= 1;
     }
     slab(st, std::true_type{});
     st ^= 1;
-    epilogue(ct / n_tiles * BM, ct % n_tiles * BN);
-    ct += nblk;
-    if (ct >= total) break;
+    epilogue(ct / ncol * BM, (grp * ncol + ct % ncol) * BN);
+    ct = tile_at(++cround);
+    if (ct < 0) break;
     // the next tile's first slab went out under this tile's last slab
     wait_loads();
     __syncthreads();
@@ -343,16 +376,38 @@ void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, c
   // workgroups per CU, so they get one workgroup per tile.
   const int tiles = ((cap_m + BM - 1) / BM) * (N / BN);
   const int grid = 2 * (BM + BN) * BK * 2 > 96 * 1024 ? std::min(tiles, cu_count()) : tiles;
+  // Column groups for the XCD-aware tile order (see the kernel): the count
+  // with the least estimated L2 fill traffic.  The activations are read once
+  // per group (xg |A|); each of the 8 XCDs reads its group's share of the
+  // weights once if that share fits its 4 MB L2, else once per round of
+  // tiles.  At the 0.6B shape with 64 requests per call this picks 1 group
+  // for the O and down projections (L2 fetch per launch 553 -> 275 MB), 2 for
+  // QKV (405 -> 267 MB) and 4 for gate/up (473 -> 394 MB); per call 25.04 ->
+  // 24.56 ms as one launch, 22.47 -> 22.31 ms as two lanes (A/B on one box,
+  // scores bit-identical).
+  constexpr double kL2Bytes = 4.0 * (1 << 20);
+  const double a_bytes = 2.0 * cap_m * K, w_bytes = 2.0 * N * K;
+  const int rounds = (tiles + grid - 1) / grid;
+  int xg = 1;
+  double best = -1.0;
+  for (int g = 1; g <= 8 && (N / BN) % g == 0; g *= 2) {
+    const double share = w_bytes / g;
+    const double est = g * a_bytes + 8.0 * share * (share <= kL2Bytes ? 1 : rounds);
+    if (best < 0 || est < best) {
+      best = est;
+      xg = g;
+    }
+  }
   const dim3 blk(WM * WN * 64);
   if (epi == EPI_BF16)
     hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
-                       ldc, dM, N, K);
+                       ldc, dM, N, K, xg);
   else if (epi == EPI_RESID)
     hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_RESID>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
-                       ldc, dM, N, K);
+                       ldc, dM, N, K, xg);
   else
     hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_SWIGLU>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
-                       ldc, dM, N, K);
+                       ldc, dM, N, K, xg);
 }
 
 
