@@ -50,6 +50,34 @@ def _compile(src: str) -> str:
     return obj
 
 
+ASAN_PATH = os.path.join(LIB_DIR, "duolm_host_asan")
+ASAN_DRIVER = os.path.join(os.path.dirname(PKG), "tests", "asan", "host_asan.cpp")
+# AddressSanitizer on host code only (device code is built as usual)
+ASAN_HOST = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+
+
+def _run(cmd, what):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        errs = "\n".join(l for l in r.stderr.splitlines() if "not a recognized feature" not in l)
+        raise RuntimeError(f"{what} failed:\n{errs}")
+
+
+def build_host_asan(objs) -> str:
+    """The host-sanitizer test driver (tests/asan/host_asan.cpp), linked with
+    api.cpp built with ASAN_HOST and the device objects as they are."""
+    api = os.path.join(BUILD_DIR, "api_asan.o")
+    drv = os.path.join(BUILD_DIR, "host_asan.o")
+    _run([hipcc(), *FLAGS, *ASAN_HOST, "-x", "hip", "-c", os.path.join(CSRC, "api.cpp"), "-o", api], "api.cpp (asan)")
+    _run([hipcc(), "-O1", "-std=c++17", *ASAN_HOST, "-I", os.path.join(os.path.dirname(PKG), "include"), "-x", "c++",
+          "-c", ASAN_DRIVER, "-o", drv], "host_asan.cpp")
+    dev = [o for o in objs if not o.endswith("api.o")]
+    tmp = ASAN_PATH + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", *ASAN_HOST, drv, api, *dev, "-o", tmp], "host_asan link")
+    os.replace(tmp, ASAN_PATH)
+    return ASAN_PATH
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
@@ -61,6 +89,8 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, LIB_PATH)
+    if os.path.exists(ASAN_DRIVER):
+        build_host_asan(objs)
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH

@@ -68,6 +68,10 @@ int fail(int code, const char* fmt, ...) {
   vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
   g_err = buf;
+  // A failed runtime call (an allocation above all) leaves HIP's per-thread
+  // last error set.  It is reported here; clear it, or the launch check of
+  // the next call would report it again.
+  if (code == DUOLM_ENOMEM || code == DUOLM_EHIP) (void)hipGetLastError();
   return code;
 }
 

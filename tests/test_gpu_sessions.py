@@ -166,6 +166,29 @@ def test_session_errors(gpu_tiny, tiny):
         r2.close()
 
 
+def test_pool_allocation_failure_leaves_ranker_usable(gpu_tiny):
+    # A pool larger than any device (2^26 pages of 32 KB: 2 TiB) fails in the
+    # device allocation itself: ENOMEM, and the ranker keeps its old pool and
+    # scores as before (a failed allocation must not leave HIP's last error
+    # behind for the next call's launch check to report).
+    cfg, _, _, _, r = gpu_tiny
+    q = synth.make_requests(1, cfg)[0]
+    want = r.score([(q.prefix, q.cands)])
+    r.kv_pool_init(4096)
+    with pytest.raises(spa.DuolmError) as ei:
+        r.kv_pool_init(64 << 26)
+    assert ei.value.code == -3 and "KV pool" in str(ei.value)
+    assert r.kv_free_pages() == 64
+    np.testing.assert_array_equal(r.score([(q.prefix, q.cands)]), want)
+    np.testing.assert_array_equal(r.score([(q.prefix, q.cands)], use_graph=False), want)
+    s = r.session()
+    try:
+        np.testing.assert_array_equal(r.step([s], [q.prefix], [q.cands]), want)
+    finally:
+        s.close()
+    assert r.kv_free_pages() == 64
+
+
 def test_sessions_in_two_lanes_equal_one(gpu_qwen):
     # a step over many users runs as two concurrent halves; one launch gives
     # the same bits
