@@ -64,7 +64,17 @@ __device__ __forceinline__ void load_lds16(const uint16_t* g, lds_u16_t* lds) {
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// wait until at most N of this wave's global->LDS loads are in flight (they
+// complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// NS: LDS stages.  NS = 2 is the persistent double-buffered loop; NS > 2 is
+// for launches whose tiles fit one per CU (one tile per workgroup).
+template <int BM, int BN, int WM, int WN, int EPI, int NS>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restrict__ A, int lda,
                                                       const uint16_t* __restrict__ W, int ldw,
                                                       void* __restrict__ Cv, int ldc,
@@ -78,7 +88,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
   static_assert(GA * NW * 8 == BM && GB * NW * 8 == BN, "tile/wave mismatch");
   static_assert(EPI != EPI_SWIGLU || NI % 2 == 0, "swiglu needs gate/up block pairs");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STAGE];
+  static_assert(NS >= 2, "stages");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * STAGE];
 
   const int M = *dM;
   const int n_tiles = N / BN;
@@ -280,6 +291,53 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
     }
   };
 
+  if constexpr (NS > 2) {
+    // One tile per workgroup, for launches whose tiles fit one per CU: an
+    // NS-stage LDS ring whose loads run NS - 1 slabs ahead of the MFMAs, so
+    // each slab's memory latency is hidden behind the slabs before it (with
+    // two stages a small launch waits about one latency on every slab).  The
+    // arithmetic is the two-stage loop's: the same k-steps in the same order.
+    static_assert((NS - 2) * NG <= 63, "loads in flight");
+    const int m0 = first / ncol * BM, n0 = (grp * ncol + first % ncol) * BN;
+    for (int sl = 0; sl < NS - 1 && sl < KT; ++sl) {
+      lk = sl;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) issue_one(g, sl);
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+      // slab kt has landed (the loads of up to NS - 2 later slabs may fly),
+      // and every wave is done with slab kt - 1, whose stage is refilled next
+      if (kt + NS - 2 < KT)
+        wait_loads_but<(NS - 2) * NG>();
+      else
+        wait_loads();
+      __syncthreads();
+      if (kt + NS - 1 < KT) {
+        lk = kt + NS - 1;
+        const int sn = lk % NS;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) issue_one(g, sn);
+      }
+      const int st = kt % NS;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) read_one(r, st, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          mfma_one(ks & 1, i);
+          if (ks + 1 < BK / 16) {
+#pragma unroll
+            for (int r = i * NR / NM; r < (i + 1) * NR / NM; ++r) read_one(r, st, ks + 1, (ks + 1) & 1);
+          }
+          fence();
+        }
+      }
+    }
+    epilogue(m0, n0);
+    return;
+  }
+
   // The last slab of a tile neither waits nor reads ahead: the next tile's
   // first slab (always issued; past the block's last tile it reloads a slab
   // of that tile into the free stage) lands under the epilogue.
@@ -366,16 +424,17 @@ int cu_count() {
   return n;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NS = 2>
 void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, const uint16_t* W, int ldw,
                 void* C, int ldc, const int32_t* dM, int N, int K) {
-  // Persistent workgroups for the large tiles, whose LDS stages (112-128 KB)
-  // allow one workgroup per CU: one per tile up to one per CU (a two-lane
-  // split still gives each launch the whole chip: capping it at its share of
-  // the CUs measured 6% slower per call).  Smaller tiles fit several
-  // workgroups per CU, so they get one workgroup per tile.
+  // Two stages: persistent workgroups for the large tiles, whose LDS stages
+  // (112-128 KB) allow one workgroup per CU: one per tile up to one per CU (a
+  // two-lane split still gives each launch the whole chip: capping it at its
+  // share of the CUs measured 6% slower per call).  Smaller tiles fit several
+  // workgroups per CU, so they get one workgroup per tile.  Deeper rings:
+  // one workgroup per tile.
   const int tiles = ((cap_m + BM - 1) / BM) * (N / BN);
-  const int grid = 2 * (BM + BN) * BK * 2 > 96 * 1024 ? std::min(tiles, cu_count()) : tiles;
+  const int grid = NS == 2 && 2 * (BM + BN) * BK * 2 > 96 * 1024 ? std::min(tiles, cu_count()) : tiles;
   // Column groups for the XCD-aware tile order (see the kernel): the count
   // with the least estimated L2 fill traffic.  The activations are read once
   // per group (xg |A|); each of the 8 XCDs reads its group's share of the
@@ -400,13 +459,13 @@ void launch_cfg(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, c
   }
   const dim3 blk(WM * WN * 64);
   if (epi == EPI_BF16)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_BF16, NS>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
                        ldc, dM, N, K, xg);
   else if (epi == EPI_RESID)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_RESID>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_RESID, NS>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
                        ldc, dM, N, K, xg);
-  else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_SWIGLU>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
+  else if constexpr ((BN / WN / 32) % 2 == 0)  // the chooser never asks others for SwiGLU
+    hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI_SWIGLU, NS>), dim3(grid), blk, 0, s, A, lda, W, ldw, C,
                        ldc, dM, N, K, xg);
 }
 
@@ -441,8 +500,16 @@ bool launch_gemm(hipStream_t s, int epi, int cap_m, const uint16_t* A, int lda, 
     launch_cfg<192, 256, 2, 4>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else if (nt && tiles256 >= ncu)
     launch_cfg<256, 256, 4, 2>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
-  else if (N % 128 == 0 && tiles128 >= 128)
+  else if (N % 128 == 0 && tiles128 >= ncu)
     launch_cfg<128, 128, 2, 2>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+  // Fewer tiles than CUs: one workgroup per CU, so a deep LDS ring fits
+  // (4 x 32 KB or 8 x 16 KB) and hides the memory latency of each slab.
+  // 64 x 64 tiles of four 32 x 32 waves double the workgroups of a narrow
+  // projection; SwiGLU needs gate/up block pairs in a wave, so 128 x 128.
+  else if (N % 128 == 0 && (tiles128 >= ncu / 4 || epi == EPI_SWIGLU))
+    launch_cfg<128, 128, 2, 2, 4>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
+  else if (N % 128 == 0)
+    launch_cfg<64, 64, 2, 2, 8>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   else
     launch_cfg<64, 64, 1, 1>(s, epi, cap_m, A, lda, W, ldw, C, ldc, dM, N, K);
   return true;

@@ -28,8 +28,12 @@ def to_dev(a):
 
 
 GEMM_SHAPES = [
-    (1, 64, 64), (77, 256, 128), (300, 768, 384), (513, 4096, 1024),   # 64x64 tiles, ragged M
-    (4100, 1024, 2048), (1500, 3072, 1024),                          # 128x128 tiles
+    (1, 64, 64),                                                     # 64x64 tiles of one wave (N % 128 != 0)
+    # fewer tiles than CUs: 64x64 tiles of four waves (128x128 for SwiGLU) on
+    # an 8-stage LDS ring; K from one slab (64) to 48 slabs, ragged M
+    (77, 256, 128), (300, 768, 384), (200, 128, 64), (40, 1024, 3072),
+    (513, 4096, 1024),                                               # 128x128 tiles, 4-stage ring
+    (4100, 1024, 2048), (1500, 3072, 1024),                          # 128x128 tiles, two stages
     (4096, 4096, 1024), (4133, 6144, 1024),                          # 256x256 tiles, ragged tail
     (16500, 1024, 256), (12000, 2048, 64),                           # 256-row tiles, or 192-row for the residual epilogue
 ]
