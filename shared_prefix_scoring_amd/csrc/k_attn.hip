@@ -209,26 +209,43 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   constexpr int KPI = 1024 / (2 * HD);        // keys per load instruction
   constexpr int NLI = BKV / KPI;              // instructions per tile and matrix
   constexpr int LPW = (2 * NLI + NW - 1) / NW;  // instructions per wave (K and V)
+  // Per-lane parts of each load, fixed for the item: the key within the tile
+  // and the element offset of its chunk from the tile's first key row.  A
+  // full tile then adds one wave-uniform row offset; only a tile that runs
+  // past kend clamps its keys.
+  const size_t key_stride = item.pt >= 0 ? (size_t)Hkv * HD : (size_t)ld;
+  int k_in[LPW];
+  size_t l_off[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int ins = wave + j * NW;  // wave-uniform
+    const bool isv = ins >= NLI;
+    const int key = (isv ? ins - NLI : ins) * KPI + lane / CPR;
+    const int slot = lane % CPR;
+    const int dc = slot ^ (isv ? vswz(key) : key % CPR);
+    k_in[j] = key;
+    l_off[j] = (size_t)key * key_stride +
+               (item.pt >= 0 ? (size_t)(isv ? kPageRows * Hkv * HD : 0) + g * HD : (size_t)(isv ? vcol : kcol)) +
+               dc * 8;
+  }
   auto issue = [&](int k0, auto st) {
     lds_u16_t* const dK = (lds_u16_t*)(lds_void_t*)kt(st);
     lds_u16_t* const dV = (lds_u16_t*)(lds_void_t*)vt(st);
+    const uint16_t* tbase;  // the tile's first key row
+    if (item.pt >= 0) {
+      const int pg = b.pages[item.pt + k0 / kPageRows];  // uniform over the tile
+      tbase = b.kv + (int64_t)pg * b.page_stride + (size_t)(k0 % kPageRows) * (Hkv * HD);
+    } else {
+      tbase = QKV + (size_t)(item.koff + k0) * ld;
+    }
+    const bool full = k0 + BKV <= kend;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int ins = wave + j * NW;  // wave-uniform
       if (ins < 2 * NLI) {
         const bool isv = ins >= NLI;
-        const int key = (isv ? ins - NLI : ins) * KPI + lane / CPR;
-        const int slot = lane % CPR;
-        const int dc = slot ^ (isv ? vswz(key) : key % CPR);
-        const int kr = min(k0 + key, kend - 1);
-        const uint16_t* src;
-        if (item.pt >= 0) {
-          const int pg = b.pages[item.pt + k0 / kPageRows];  // uniform over the tile
-          const uint16_t* page = b.kv + (int64_t)pg * b.page_stride;
-          src = page + (isv ? kPageRows * Hkv * HD : 0) + (size_t)(kr % kPageRows) * (Hkv * HD) + g * HD + dc * 8;
-        } else {
-          src = QKV + (size_t)(item.koff + kr) * ld + (isv ? vcol : kcol) + dc * 8;
-        }
+        const uint16_t* src = tbase + l_off[j];
+        if (!full) src += (ptrdiff_t)(min(k0 + k_in[j], kend - 1) - (k0 + k_in[j])) * (ptrdiff_t)key_stride;
         lds_u16_t* dst = (isv ? dV : dK) + (isv ? ins - NLI : ins) * KPI * HD;
         load_lds16(src, dst);
       }

@@ -166,39 +166,57 @@ __global__ __launch_bounds__(256) void k_qk_rope(uint16_t* __restrict__ QKV, int
     g_k[e] = gk[t * 8 + e];
   }
   uint16_t* rowp = QKV + (size_t)row * ld;
-  for (int head = slot; head < H + Hkv; head += slots) {
-    const bool isq = head < H;
-    uint16_t* p = rowp + (isq ? head * hd : H * hd + (head - H) * hd) + t * 8;
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float x[8];
+  // The row is updated in place, so a head's load could not otherwise be
+  // issued before the previous head's store: the heads' loads go out
+  // together, kMaxIt at a time, then each head is normalised, rotated and
+  // stored (heads are disjoint, and each element's arithmetic is unchanged).
+  constexpr int kMaxIt = 8;
+  auto head_ptr = [&](int head) {
+    return rowp + (head < H ? head * hd : H * hd + (head - H) * hd) + t * 8;
+  };
+  for (int h0 = slot; h0 < H + Hkv; h0 += kMaxIt * slots) {
+    uint4 vin[kMaxIt];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xffffu));
-      x[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+    for (int it = 0; it < kMaxIt; ++it) {
+      const int head = h0 + it * slots;
+      if (head < H + Hkv) vin[it] = *reinterpret_cast<const uint4*>(head_ptr(head));
     }
-    float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-    for (int m = tph >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, tph);
-    const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
-    float y[8], q[8];
+    for (int it = 0; it < kMaxIt; ++it) {
+      const int head = h0 + it * slots;
+      if (head >= H + Hkv) break;
+      const bool isq = head < H;
+      const uint4 v = vin[it];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * (isq ? g_q[e] : g_k[e]);
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xffffu));
+        x[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+      }
+      float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = __shfl_xor(y[e], half_t, tph);  // partner dims (i +- hd/2)
-    float o[8];
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+      for (int m = tph >> 1; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, tph);
+      const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
+      float y[8], q[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // first half: x1 cos - x2 sin; second half: x2 cos + x1 sin
-      o[e] = lo ? y[e] * c[e].x - q[e] * c[e].y : y[e] * c[e].x + q[e] * c[e].y;
+      for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * (isq ? g_q[e] : g_k[e]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = __shfl_xor(y[e], half_t, tph);  // partner dims (i +- hd/2)
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // first half: x1 cos - x2 sin; second half: x2 cos + x1 sin
+        o[e] = lo ? y[e] * c[e].x - q[e] * c[e].y : y[e] * c[e].x + q[e] * c[e].y;
+      }
+      uint4 out;
+      out.x = pack_bf16x2(o[0], o[1]);
+      out.y = pack_bf16x2(o[2], o[3]);
+      out.z = pack_bf16x2(o[4], o[5]);
+      out.w = pack_bf16x2(o[6], o[7]);
+      *reinterpret_cast<uint4*>(head_ptr(head)) = out;
     }
-    uint4 out;
-    out.x = pack_bf16x2(o[0], o[1]);
-    out.y = pack_bf16x2(o[2], o[3]);
-    out.z = pack_bf16x2(o[4], o[5]);
-    out.w = pack_bf16x2(o[6], o[7]);
-    *reinterpret_cast<uint4*>(p) = out;
   }
 }
 
