@@ -642,7 +642,8 @@ def headline(args, cfg, w, ranker):
     ranker.set_profiling([])
     if br.launches == 0 or any(st.launches == 0 for st in stats.values()):
         raise RuntimeError("no timed launches recorded for the roofline kernels")
-    per = {"qkv": gemm_roofline(stats, ["gemm_qkv"], "k_gemm, QKV projection (bf16 store)"),
+    per = {"all": gemm_roofline(stats, gemm_classes, "k_gemm, all four projections of every layer"),
+           "qkv": gemm_roofline(stats, ["gemm_qkv"], "k_gemm, QKV projection (bf16 store)"),
            "o": gemm_roofline(stats, ["gemm_o"], "k_gemm, O projection (+ fp32 residual)"),
            "gateup": gemm_roofline(stats, ["gemm_gateup"], "k_gemm, gate/up projection (+ SwiGLU)"),
            "down": gemm_roofline(stats, ["gemm_down"], "k_gemm, down projection (+ fp32 residual)")}
