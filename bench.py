@@ -15,7 +15,9 @@ kernel and of every projection GEMM and of candidate-branch attention (timed
 live with HIP events on the launching stream); the pages' comparison points
 measured here (one-request latency, MIS against independent scoring at C = 1
 and C = 64, graph replay against eager launch at C = 1, 8 and 64); an open-loop
-Poisson run; and the CPU oracle's rate on bounded samples.
+Poisson run; and the CPU oracle's rate on bounded samples, with the GPU's
+scores of the oracle's sample requests compared against it (largest relative
+error, and requests whose top ten candidates are not the oracle's, in order).
 
 Before each phase a 16-byte copy kernel (k_copy) is launched as a marker, so
 that a rocprofv3 kernel trace of this run can be cut into phases (python -m
@@ -109,14 +111,23 @@ def host_cpu():
     return {"model": model, "os_cpu_count": os.cpu_count(), "blas_threads": blas}
 
 
-def cpu_baseline(cfg, w, pool, budget_s):
+def strict_top10_swaps(got, ref):
+    """1 if the GPU's ten best candidates, in order, differ from the oracle's."""
+    g = np.argsort(-np.asarray(got, np.float64), kind="stable")[:10]
+    r = np.argsort(-np.asarray(ref, np.float64), kind="stable")[:10]
+    return int(not np.array_equal(g, r))
+
+
+def cpu_baseline(cfg, w, pool, budget_s, ranker=None):
     """The float64 oracle as written (untuned), on the host cores:
       - value: consecutive requests of the headline pool until about budget_s
         of wall time has been spent;
       - the one-request workload (L = 452, K = 100), five repeats;
       - brute-force independent scoring (one causal forward per candidate):
         the tiny workload in full, and a stated subset of the one-request
-        workload's candidates (the full request is ~100x the subset).
+        workload's candidates (the full request is ~100x the subset);
+      - with `ranker`, the GPU's scores of the sampled requests against the
+        oracle's (gpu_vs_oracle).
     The oracle's item table is its own export of the same encoder outputs;
     building it and the oracle's weights is not timed."""
     import synth
@@ -130,9 +141,10 @@ def cpu_baseline(cfg, w, pool, budget_s):
     model = OracleModel.from_arrays(cfg, w, D)
     hc = host_cpu()
     n_scores, n_req = 0, 0
+    refs = []
     t0 = time.perf_counter()
     for r in pool:
-        oracle_mis(model, r.prefix, r.cands)
+        refs.append(oracle_mis(model, r.prefix, r.cands))
         n_scores += r.K
         n_req += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -141,6 +153,20 @@ def cpu_baseline(cfg, w, pool, budget_s):
     out = {"value": n_scores / dt, "unit": "candidate scores/s", "cores": hc["blas_threads"], "kind": "oracle",
            "sample": f"{n_req} consecutive requests ({n_scores} candidate scores) of the headline pool, one at a "
                      f"time, float64 NumPy, {dt:.1f} s", "host": hc}
+    if ranker is not None:
+        # the same requests scored on the GPU (one call) against the oracle's
+        # scores: |error| relative to max(1, |s|), and requests whose top ten
+        # (in order) differ from the oracle's
+        got = ranker.score([(r.prefix, r.cands) for r in pool[:n_req]])
+        errs, swaps, o = [], 0, 0
+        for r, ref in zip(pool[:n_req], refs):
+            g = got[o:o + r.K]
+            o += r.K
+            errs.append(float(np.max(np.abs(g - ref) / np.maximum(1.0, np.abs(ref)))))
+            swaps += strict_top10_swaps(g, ref)
+        out["gpu_vs_oracle"] = {"requests": n_req, "max_rel_err": round(max(errs), 5),
+                                "requests_with_strict_top10_swap": swaps,
+                                "tolerance": "2e-2 relative to max(1, |s|)"}
     (r2,) = synth.make_requests(2, cfg)
     ts = []
     for _ in range(5):
@@ -726,7 +752,7 @@ def headline(args, cfg, w, ranker):
                             "warmup": "an untimed open loop of half as many requests, other arrivals"}
     if args.cpu_baseline_s > 0:
         log("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(cfg, w, pool, args.cpu_baseline_s)
+        out["cpu_baseline"] = cpu_baseline(cfg, w, pool, args.cpu_baseline_s, ranker)
     return out
 
 
