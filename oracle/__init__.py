@@ -1,7 +1,7 @@
 """CPU oracle for the DuoLM multi-item-scoring (MIS) ranker forward.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or run
-anything in this package: only the test-suite, the graft smoke check and the
+anything in this package: only the test-suite, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of the benchmark use it.  It shares no code with the HIP
 library and imports nothing from it.
 
