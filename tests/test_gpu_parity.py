@@ -197,6 +197,25 @@ def test_graph_matches_eager_and_repeats(gpu_qwen):
     np.testing.assert_array_equal(r.score(reqs, use_graph=True), eager)
 
 
+def test_batch_composition_sweep(gpu_qwen):
+    # Random sub-batches of the 64-request headline batch, sized to cross every
+    # GEMM tile regime (deep LDS rings below one tile per CU, two-stage and
+    # persistent tiles above) and the two-lane threshold, in graph and eager
+    # launches and with one or two lanes: each request's scores equal its slice
+    # of the full batch bit for bit.
+    cfg, _, _, _, r = gpu_qwen
+    reqs = reqs_of(cfg, 3, n=64)
+    full = split(r.score(reqs), reqs)
+    rng = np.random.default_rng(11)
+    for n in (1, 2, 5, 13, 40):
+        pick = rng.choice(64, size=n, replace=False)
+        sub = [reqs[i] for i in pick]
+        for graph, lanes in ((True, 0), (False, 0), (True, 1)):
+            got = split(r.score(sub, use_graph=graph, max_lanes=lanes), sub)
+            for j, i in enumerate(pick):
+                np.testing.assert_array_equal(got[j], full[i])
+
+
 def test_permutation_and_leakage(gpu_tiny):
     cfg, _, _, _, r = gpu_tiny
     (p, c), = reqs_of(cfg, 1)
