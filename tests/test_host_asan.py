@@ -32,6 +32,8 @@ def test_packer_under_asan():
     if not os.path.exists(EXE):
         from shared_prefix_scoring_amd import build
         build.build()
+    if not os.path.exists(EXE):
+        pytest.skip("the toolchain could not build the host-sanitizer driver (see the build warning)")
     r = _run(["pack"], "detect_leaks=1:abort_on_error=1", 600)
     assert r.returncode == 0, r.stderr[-4000:]
     assert r.stdout.startswith("ok pack"), r.stdout
