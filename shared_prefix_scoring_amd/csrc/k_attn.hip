@@ -58,9 +58,13 @@ __device__ __forceinline__ v4i16_t lds_read_tr16(const lds_u16_t* p) {
 }
 
 // One instantiation serves both row kinds, so a candidate row and a causal
-// row run the very same instruction sequence.  A launch may carry both kinds:
-// blocks [0, pcap) take prefix tiles, the rest branch tiles, so the two run
+// row run the very same instruction sequence.  A launch may carry both kinds,
 // side by side on the chip (both are latency-bound, one workgroup per CU).
+// The grid is one-dimensional and item-major: block b takes KV head b % Hkv
+// of item b / Hkv, branch items [0, bcap) first, then the prefix items, each
+// list longest first.  So all heads of the longest items go out first and
+// the launch ends on short items (dispatching head by head had left the
+// longest items' last heads for the end: branch launch 48.9 -> 41.7 us).
 // V chunk swizzle: the four consecutive keys of a transpose read land in four
 // different 16-chunk quarters of the bank space.
 template <int CPR>
@@ -78,15 +82,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // exceeds it by more than that.
 constexpr float kLazyTau = 8.0f;
 
-// BRANCH_ONLY: a launch of branch tiles alone (pcap = 0), compiled as an
+// BRANCH_ONLY: a launch of branch tiles alone (no prefix tiles), compiled as an
 // instantiation of its own so that profiles tell it apart from the launches
 // that carry prefix tiles; every row runs the same arithmetic in both.
 template <int HD, int NW, int BKV, bool BRANCH_ONLY>
 __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ QKV, int ld,
                                                  uint16_t* __restrict__ O, int ldo, DevBatch b, int H,
-                                                 int Hkv, float scale_log2, int pcap) {
-  const bool BRANCH = BRANCH_ONLY || (int)blockIdx.x >= pcap;
-  const int idx = BRANCH ? (int)blockIdx.x - pcap : (int)blockIdx.x;
+                                                 int Hkv, float scale_log2, int bcap) {
+  const int slot = (int)blockIdx.x / Hkv;
+  const bool BRANCH = BRANCH_ONLY || slot < bcap;
+  const int idx = BRANCH ? slot : slot - bcap;
   constexpr int NKS = HD / 16;         // k-steps of the QK^T product
   constexpr int NDB = HD / 32;         // 32-dim blocks of the output
   constexpr int CPR = HD / 8;          // 16-byte chunks per key row / per query column
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(const uint16_t* __restrict__ Q
   struct {
     int row_off, L, K;
   } const sd = {item.row_off, item.L, item.K};
-  const int g = blockIdx.y;  // KV head
+  const int g = (int)blockIdx.x % Hkv;  // KV head
   const int G = H / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -490,13 +495,13 @@ constexpr int BKV = 64;  // keys per streamed tile
 template <int HD>
 void launch_hd(hipStream_t s, int cap_p, int cap_b, const uint16_t* QKV, int ld, uint16_t* O, int ldo,
                DevBatch b, int H, int Hkv, float scale_log2) {
-  const dim3 grid(cap_p + cap_b, Hkv);
+  const dim3 grid((cap_p + cap_b) * Hkv);
   if (cap_p == 0)
     hipLaunchKernelGGL((k_attn<HD, NW, BKV, true>), grid, dim3(NW * 64), 0, s, QKV, ld, O, ldo, b, H, Hkv,
-                       scale_log2, 0);
+                       scale_log2, cap_b);
   else
     hipLaunchKernelGGL((k_attn<HD, NW, BKV, false>), grid, dim3(NW * 64), 0, s, QKV, ld, O, ldo, b, H, Hkv,
-                       scale_log2, cap_p);
+                       scale_log2, cap_b);
 }
 
 }  // namespace
