@@ -27,7 +27,6 @@ GEMM rooflines), 4 capture of the split-attention graphs, 5 the
 branch-attention timing, then the comparison points.
 """
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -56,11 +55,8 @@ def log(msg):
 
 
 def src_hash(*names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "shared_prefix_scoring_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from shared_prefix_scoring_amd.rocprof_summary import code_hash
+    return code_hash(names)
 
 
 GEMM_SRC = ("k_gemm.hip", "common.h", "launch.h")

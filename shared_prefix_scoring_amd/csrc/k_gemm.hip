@@ -25,10 +25,13 @@
 //     a wait for all outstanding LDS traffic; with the loads out of its view
 //     each k-step waits only for the fragments its first MFMAs need, and the
 //     kernel waits for the loads itself (vmcnt) before the stage barrier;
-//   * persistent: at most one workgroup per CU, each walking the tiles
-//     blockIdx.x, + gridDim.x, ...; a tile's last slab loads the next tile's
-//     first slab into the free stage, and that load lands while the tile's
-//     epilogue runs (no relaunch, no exposed first-slab latency);
+//   * persistent: at most one workgroup per CU, each walking its tiles
+//     round by round in an XCD-aware order (see the kernel); a tile's last
+//     slab loads the next tile's first slab into the free stage, and that
+//     load lands while the tile's epilogue runs (no relaunch, no exposed
+//     first-slab latency);
+//   * a launch with fewer tiles than CUs runs one tile per workgroup on a
+//     deeper LDS ring (NS stages), its loads several slabs ahead;
 //   * the k loop order is fixed and there is no split-K, so every output row
 //     is computed by the same instruction sequence whatever M is or where the
 //     row sits: results are batch invariant;

@@ -27,7 +27,7 @@
         and a down projection over all rows: weights, activations in, the
         fp32 residual read and written), gemm_gateup or gemm_qkv (weights,
         activations in, bf16 output).  The JSON also records a hash of the
-        kernel's sources, so that a benchmark on changed kernels reports no
+        kernel's code (comments aside), so that a benchmark on changed kernels reports no
         traffic.
 """
 from __future__ import annotations
@@ -162,13 +162,25 @@ SOURCES = {"attn_branch": ("k_attn.hip", "common.h", "launch.h"),
            "gemm_qkv": ("k_gemm.hip", "common.h", "launch.h")}
 
 
-def src_hash(which: str) -> str:
+def code_hash(names) -> str:
+    """Hash of the kernel sources with comments, blank lines and indentation
+    removed, so that a change of code (not of comments) makes recorded
+    counters stale."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for n in SOURCES[which]:
-        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", n), "rb") as f:
-            h.update(f.read())
+    for n in names:
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", n)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.split("\n"):
+            line = re.sub(r"//.*$", "", line).strip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
+
+
+def src_hash(which: str) -> str:
+    return code_hash(SOURCES[which])
 
 
 def traffic(d: str, kernel: str, which: str) -> None:
