@@ -22,8 +22,8 @@ error, and requests whose top ten candidates are not the oracle's, in order).
 Before each phase a 16-byte copy kernel (k_copy) is launched as a marker, so
 that a rocprofv3 kernel trace of this run can be cut into phases (python -m
 shared_prefix_scoring_amd.rocprof_summary trace DIR): 1 the serving timed
-region, 2 capture of the one-lane graphs, 3 the one-lane timed region (the
-GEMM rooflines), 4 capture of the split-attention graphs, 5 the
+region, 2 a one-lane eager warm-up, 3 the one-lane eager timed region (the
+GEMM rooflines), 4 a warm-up of the split-attention launches, 5 the
 branch-attention timing, then the comparison points.
 """
 import argparse
@@ -607,13 +607,13 @@ def headline(args, cfg, w, ranker):
         ranker.score_dev(b[1], b[2], b[0].data_ptr(), b[3].data_ptr(), use_graph=graph, stream=stream,
                          max_lanes=lanes, mode=mode)
 
-    def timed_steps(lanes):
+    def timed_steps(lanes, graph=use_graph):
         lat = []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.warmup, n_calls):
             ts = time.perf_counter()
-            call(batches[i], lanes)
+            call(batches[i], lanes, graph)
             lat.append(time.perf_counter() - ts)
         torch.cuda.synchronize()
         return time.perf_counter() - t0, lat
@@ -633,32 +633,34 @@ def headline(args, cfg, w, ranker):
     n_scores = sum(int(b[2].sum()) for b in batches[args.warmup:])
     rows = [int(b[1].sum() + b[2].sum()) for b in batches[args.warmup:]]
     value = n_scores / dt
-    # phase 2: the projection GEMMs timed live with HIP event-record nodes
-    # around every launch, over a second timed region of the same steps run
-    # as one launch per call, so each kernel has the chip to itself (with two
-    # concurrent halves a launch's duration would include time the other
-    # half's kernels share the chip)
+    # phases 2-3: the projection GEMMs timed live with HIP events recorded on
+    # the launching stream around every launch, over a second timed region of
+    # the same steps run as one eager launch per call, so each kernel has the
+    # chip to itself (with two concurrent halves a launch's duration would
+    # include time the other half's kernels share the chip; event-record
+    # nodes inside a graph add a few more microseconds per launch than events
+    # recorded between eager launches)
     log("one-lane timed region (GEMM timing)")
     gemm_classes = ["gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down"]
     ranker.set_profiling(gemm_classes)
-    marker()  # phase 2: capture of the one-lane graphs
-    if use_graph:
-        for i in range(args.warmup, n_calls):
-            call(batches[i], 1)
-        ranker.set_profiling(gemm_classes)  # reset the counters, keep the graphs
+    marker()  # phase 2: one-lane warm-up
+    for i in range(args.warmup, n_calls):
+        call(batches[i], 1, False)
+    ranker.set_profiling(gemm_classes)  # reset the counters
     marker()  # phase 3: the one-lane timed region
-    dt1, _ = timed_steps(1)
+    dt1, _ = timed_steps(1, graph=False)
     stats = {c: ranker.kernel_stats(c) for c in gemm_classes}
-    # phase 3: candidate-branch attention, one lane, its tiles launched on
-    # their own (prefix tiles in a launch of their own beside them)
+    # phases 4-5: candidate-branch attention, one eager launch per call, its
+    # tiles launched on their own (prefix tiles in a launch of their own
+    # beside them)
     ranker.set_profiling(["attn_branch"])
-    marker()  # phase 4: capture of the split-attention graphs
+    marker()  # phase 4: warm-up of the split-attention launches
     for i in range(args.warmup, min(n_calls, args.warmup + 10)):
-        call(batches[i], 1)
+        call(batches[i], 1, False)
     ranker.set_profiling(["attn_branch"])
     marker()  # phase 5: the branch-attention timing
     for i in range(args.warmup, min(n_calls, args.warmup + 10)):
-        call(batches[i], 1)
+        call(batches[i], 1, False)
     torch.cuda.synchronize()
     br = ranker.kernel_stats("attn_branch")
     ranker.set_profiling([])
@@ -677,9 +679,9 @@ def headline(args, cfg, w, ranker):
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     roof = dict(kernels[dom])
     roof["traffic"] = traffic_from_profile(dom, src_hash(*GEMM_SRC))
-    roof["timed"] = ("a second timed region over the same steps, one launch per call (no concurrent halves), HIP "
-                     "event-record nodes around every projection GEMM launch; the dominant kernel is the one with "
-                     "the most device time per step")
+    roof["timed"] = ("a second timed region over the same steps, one eager launch per call (no concurrent halves), "
+                     "HIP events recorded on the launching stream around every projection GEMM launch; the dominant "
+                     "kernel is the one with the most device time per step")
     roof["ms_per_step"] = round(roof["ms_per_step"] / args.steps, 3)
     for v in per.values():
         v["ms_per_step"] = round(v["ms_per_step"] / args.steps, 3)
@@ -714,8 +716,9 @@ def headline(args, cfg, w, ranker):
         "roofline": roof,
         "gemm_rooflines": per,
         "roofline_branch_attn": {"kernel": "k_attn branch-only instantiation (candidate-branch tiles)", "bound": "hbm",
-                                 "timed": "10 one-launch calls after the timed regions, branch tiles launched on "
-                                          "their own, HIP event-record nodes around each launch",
+                                 "timed": "10 eager one-launch calls after the timed regions, branch tiles launched "
+                                          "on their own, HIP events recorded on the launching stream around each "
+                                          "launch",
                                  "achieved": round(br_ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(br_ach / PEAK_HBM_GBS, 4), "launches": br.launches,
                                  "avg_launch_ms": round(br_ms, 4), "bytes_per_launch": br_bytes,
