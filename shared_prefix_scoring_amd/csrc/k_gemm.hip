@@ -338,82 +338,81 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(const uint16_t* __restric
       }
     }
     epilogue(m0, n0);
-    return;
-  }
-
-  // The last slab of a tile neither waits nor reads ahead: the next tile's
-  // first slab (always issued; past the block's last tile it reloads a slab
-  // of that tile into the free stage) lands under the epilogue.
-  auto slab = [&](int st, auto is_last) {
-    constexpr bool last = decltype(is_last)::value;
+  } else {
+    // The last slab of a tile neither waits nor reads ahead: the next tile's
+    // first slab (always issued; past the block's last tile it reloads a slab
+    // of that tile into the free stage) lands under the epilogue.
+    auto slab = [&](int st, auto is_last) {
+      constexpr bool last = decltype(is_last)::value;
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
+      for (int ks = 0; ks < 3; ++ks) {
 #pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        mfma_one(ks & 1, i);
-        if (ks == 0) {
+        for (int i = 0; i < NM; ++i) {
+          mfma_one(ks & 1, i);
+          if (ks == 0) {
 #pragma unroll
-          for (int g = i * NG / NM; g < (i + 1) * NG / NM; ++g) issue_one(g, st ^ 1);
+            for (int g = i * NG / NM; g < (i + 1) * NG / NM; ++g) issue_one(g, st ^ 1);
+          }
+#pragma unroll
+          for (int j = i * NR / NM; j < (i + 1) * NR / NM; ++j) read_one(j, st, ks + 1, (ks + 1) & 1);
+          fence();
         }
+        if (ks == 0) advance();
+      }
 #pragma unroll
-        for (int j = i * NR / NM; j < (i + 1) * NR / NM; ++j) read_one(j, st, ks + 1, (ks + 1) & 1);
+      for (int i = 0; i < NM / 2; ++i) {
+        mfma_one(1, i);
         fence();
       }
-      if (ks == 0) advance();
-    }
-#pragma unroll
-    for (int i = 0; i < NM / 2; ++i) {
-      mfma_one(1, i);
-      fence();
-    }
-    if constexpr (!last) {
-      wait_loads();
-      __syncthreads();
-    }
-    fence();
-#pragma unroll
-    for (int i = NM / 2; i < NM; ++i) {
-      mfma_one(1, i);
       if constexpr (!last) {
-        const int i2 = i - NM / 2;
-#pragma unroll
-        for (int j = i2 * NR / (NM / 2); j < (i2 + 1) * NR / (NM / 2); ++j) read_one(j, st ^ 1, 0, 0);
+        wait_loads();
+        __syncthreads();
       }
       fence();
-    }
-  };
+#pragma unroll
+      for (int i = NM / 2; i < NM; ++i) {
+        mfma_one(1, i);
+        if constexpr (!last) {
+          const int i2 = i - NM / 2;
+#pragma unroll
+          for (int j = i2 * NR / (NM / 2); j < (i2 + 1) * NR / (NM / 2); ++j) read_one(j, st ^ 1, 0, 0);
+        }
+        fence();
+      }
+    };
 
 #pragma unroll
-  for (int g = 0; g < NG; ++g) issue_one(g, 0);
-  advance();
-  wait_loads();
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < NR; ++j) read_one(j, 0, 0, 0);
-  int st = 0;
-  for (int ct = first, cround = 0;;) {
-    for (int kt = 0; kt + 1 < KT; ++kt) {
-      slab(st, std::false_type{});
-      st ^= 1;
-    }
-    slab(st, std::true_type{});
-    st ^= 1;
-    epilogue(ct / ncol * BM, (grp * ncol + ct % ncol) * BN);
-    ct = tile_at(++cround);
-    if (ct < 0) break;
-    // the next tile's first slab went out under this tile's last slab
+    for (int g = 0; g < NG; ++g) issue_one(g, 0);
+    advance();
     wait_loads();
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < NR; ++j) read_one(j, st, 0, 0);
+    for (int j = 0; j < NR; ++j) read_one(j, 0, 0, 0);
+    int st = 0;
+    for (int ct = first, cround = 0;;) {
+      for (int kt = 0; kt + 1 < KT; ++kt) {
+        slab(st, std::false_type{});
+        st ^= 1;
+      }
+      slab(st, std::true_type{});
+      st ^= 1;
+      epilogue(ct / ncol * BM, (grp * ncol + ct % ncol) * BN);
+      ct = tile_at(++cround);
+      if (ct < 0) break;
+      // the next tile's first slab went out under this tile's last slab
+      wait_loads();
+      __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int j = 0; j < NR; ++j) read_one(j, st, 0, 0);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+    }
+    wait_loads();  // no load into LDS outlives the workgroup
   }
-  wait_loads();  // no load into LDS outlives the workgroup
 }
 
 int cu_count() {
