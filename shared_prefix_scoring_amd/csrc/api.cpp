@@ -1188,7 +1188,19 @@ int run_plans(duolm_ranker* R, const std::vector<Plan>& plans, const int32_t* id
     HIP_TRY(hipEventRecord(R->lanes[li].done, R->lanes[li].stream));
     HIP_TRY(hipStreamWaitEvent(s, R->lanes[li].done, 0));
   }
+  // The error flag and the scores go out behind the last launch, so the host
+  // waits once: device scores are copied by a kernel that skips the copy when
+  // the flag is set; host scores land in the pinned stage (its ids upload is
+  // earlier on this stream) and reach `out` only if the flag is clear.
   HIP_TRY(hipMemcpyAsync(R->h_err, R->d_err, 4, hipMemcpyDeviceToHost, s));
+  if (total_scores > 0) {
+    if (out_dev) {
+      launch_copy_scores(s, out, R->d_out, (int)total_scores, R->d_err);
+      HIP_TRY(hipGetLastError());
+    } else {
+      HIP_TRY(hipMemcpyAsync(R->h_stage, R->d_out, (size_t)total_scores * 4, hipMemcpyDeviceToHost, s));
+    }
+  }
   HIP_TRY(hipStreamSynchronize(s));
   if (R->prof_mask) {
     for (size_t i = 0; i < plans.size(); ++i)
@@ -1196,12 +1208,7 @@ int run_plans(duolm_ranker* R, const std::vector<Plan>& plans, const int32_t* id
     settle_spans(R, spans);
   }
   if (*R->h_err) return fail(DUOLM_ERANGE, "an id in the device batch is outside [0, V + N)");
-  if (total_scores > 0) {
-    HIP_TRY(hipMemcpyAsync(out_dev ? (void*)out : (void*)R->h_stage, R->d_out, (size_t)total_scores * 4,
-                           out_dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipStreamSynchronize(s));
-    if (!out_dev) memcpy(out, R->h_stage, (size_t)total_scores * 4);
-  }
+  if (total_scores > 0 && !out_dev) memcpy(out, R->h_stage, (size_t)total_scores * 4);
   return DUOLM_OK;
 }
 
@@ -1791,10 +1798,10 @@ int duolm_score_batch_dev_noalloc(duolm_ranker* R, const int32_t* prefix_len, co
   enqueue_forward(q, c);
   HIP_TRY(hipGetLastError());
   HIP_TRY(hipMemcpyAsync(R->h_err, R->d_err, 4, hipMemcpyDeviceToHost, s));
+  launch_copy_scores(s, d_scores, out, (int)total_scores, R->d_err);  // skipped on device when the flag is set
+  HIP_TRY(hipGetLastError());
   HIP_TRY(hipStreamSynchronize(s));
   if (*R->h_err) return fail(DUOLM_ERANGE, "an id in the device batch is outside [0, V + N)");
-  HIP_TRY(hipMemcpyAsync(d_scores, out, (size_t)total_scores * 4, hipMemcpyDeviceToDevice, s));
-  HIP_TRY(hipStreamSynchronize(s));
   return DUOLM_OK;
 }
 

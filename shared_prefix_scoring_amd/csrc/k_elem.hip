@@ -312,6 +312,25 @@ void launch_copy(hipStream_t s, void* dst, const void* src, size_t nbytes) {
 }
 
 // ---------------------------------------------------------------------------
+// The call's scores to the caller's device buffer, unless the call-wide error
+// flag is set (an out-of-range id leaves the caller's scores untouched).
+// Enqueued behind the last launch, so the host waits once per call instead of
+// reading the flag before it copies.  4-byte accesses: the caller's buffer
+// need only be float-aligned.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_copy_scores(float* __restrict__ dst, const float* __restrict__ src, int n,
+                                                     const int32_t* __restrict__ err) {
+  if (*err) return;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) dst[i] = src[i];
+}
+
+void launch_copy_scores(hipStream_t s, float* dst, const float* src, int n, const int32_t* err) {
+  if (n <= 0) return;
+  const int blocks = std::min((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_copy_scores, dim3((unsigned)blocks), dim3(256), 0, s, dst, src, n, err);
+}
+
+// ---------------------------------------------------------------------------
 // Fill n int32 values (clears flags with a kernel rather than a memset node).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_fill_i32(int32_t* __restrict__ p, int n, int32_t v) {

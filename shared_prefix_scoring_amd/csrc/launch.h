@@ -37,6 +37,8 @@ void launch_qk_rope(hipStream_t s, int cap_rows, uint16_t* QKV, int ld, const Ca
 void launch_head(hipStream_t s, int cap_scores, const float* X, DevBatch b, const float* gf,
                  const float* w, float* scores, int d, float eps);
 void launch_copy(hipStream_t s, void* dst, const void* src, size_t nbytes);
+// dst[0, n) = src[0, n) unless *err is nonzero
+void launch_copy_scores(hipStream_t s, float* dst, const float* src, int n, const int32_t* err);
 void launch_fill_i32(hipStream_t s, int32_t* p, int n, int32_t v);
 // Store the K and V of the new prefix rows of session sequences into their
 // pages (the layer's block, b.kv).  Rows of other sequences are skipped.
