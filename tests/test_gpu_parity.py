@@ -487,3 +487,42 @@ def test_two_lanes_equal_one_launch(gpu_qwen):
     np.testing.assert_array_equal(r.score(small, mode=IND), r.score(small, mode=IND, max_lanes=1))
     with pytest.raises(spa.DuolmError):
         r.score(small, max_lanes=3)
+
+
+def test_two_lane_out_of_range_id_leaves_scores_untouched(gpu_qwen):
+    # a 64-request call runs as two concurrent halves; an out-of-range id in
+    # either half must fail the whole call with ERANGE and write no score
+    # (the halves' gathers share one device flag, read before any score is
+    # handed over), and the next valid call must still be exact
+    cfg, _, _, _, r = gpu_qwen
+    reqs = reqs_of(cfg, 3, n=64)
+    ids, L, K = synth.pack_ids([synth.Request(np.asarray(p), np.asarray(c)) for p, c in reqs])
+    want = r.score(reqs)
+    n_first = int(L[0] + K[0])                       # first request's ids: first half
+    last_off = int((L + K)[:-1].sum())               # last request's first id: second half
+    for pos in (n_first - 1, last_off + 1):
+        for g in (True, False):
+            bad = ids.copy()
+            bad[pos] = cfg.vocab + cfg.n_vid
+            d_bad = torch.from_numpy(bad).cuda()
+            d_s = torch.full((int(K.sum()),), -7.0, device="cuda")
+            with pytest.raises(spa.DuolmError) as e:
+                r.score_dev(L, K, d_bad.data_ptr(), d_s.data_ptr(), use_graph=g)
+            assert e.value.status == "ERANGE"
+            assert torch.all(d_s == -7.0)
+            bad_reqs = list(reqs)
+            p, c = bad_reqs[0 if pos < n_first else -1]
+            p = np.array(p, np.int32)
+            c = np.array(c, np.int32)
+            if pos < n_first:
+                c[-1] = cfg.vocab + cfg.n_vid
+            else:
+                p[1] = cfg.vocab + cfg.n_vid
+            bad_reqs[0 if pos < n_first else -1] = (p, c)
+            with pytest.raises(spa.DuolmError) as e:
+                r.score(bad_reqs, use_graph=g)
+            assert e.value.status == "ERANGE"
+    d_ids = torch.from_numpy(ids).cuda()
+    d_s = torch.empty(int(K.sum()), device="cuda")
+    r.score_dev(L, K, d_ids.data_ptr(), d_s.data_ptr())
+    np.testing.assert_array_equal(d_s.cpu().numpy(), want)
